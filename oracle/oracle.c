@@ -1,0 +1,198 @@
+/*
+ * oracle.c -- plain fp64 CPU checker for one tensor-parallel shard of a
+ * transformer layer.  TEST INFRASTRUCTURE ONLY: the GPU library never links,
+ * loads or calls this file; only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg do.
+ *
+ * Every routine is the written-out definition of what the shard computes,
+ * evaluated in double precision with no intermediate rounding and no
+ * blocking: sums run over k in increasing order.  OpenMP only spreads the
+ * independent output rows over host threads; it changes no arithmetic.
+ *
+ * Sources (the pages' notation is kept):
+ *  - column split X[s,h] . W(i)[h,h'/t] and row split X(i)[s,h'/t] . W(i)[h'/t,h]:
+ *    "7.3 模型并行与张量并行" (LLM internals book) §7.3.2, and the CMU 11-868
+ *    lecture 16 notes §5.1;
+ *  - MLP Z = act(X.A).B with A column-split, B row-split, one sum of partials:
+ *    lecture 16 notes §5.2, book §7.3.2 worked example;
+ *  - backward dY.W2^T, activation mask, .W1^T per card, partial dX summed:
+ *    book §7.3.3;
+ *  - head-split Q/K/V and row-split W_O, SwiGLU gate/up column split with an
+ *    elementwise product and row-split down projection: book §7.3.4;
+ *  - vocab-split embedding (zero vector for tokens outside the shard) and
+ *    vocab-parallel cross entropy (max, sum of exponentials, target logit):
+ *    book §7.3.4 and lecture 16 notes §5.5.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stddef.h>
+
+/* ---------------------------------------------------------------------- */
+/* dense product                                                           */
+/* ---------------------------------------------------------------------- */
+
+/* C[i,j] = sum_{k=0}^{K-1} A(i,k) * B(k,j), with A(i,k) = A[i*a_rs + k*a_cs]
+ * and B(k,j) = B[k*b_rs + j*b_cs]; C is row-major [M,N].  The strides let
+ * the same definition express X.W, dY.W^T and X^T.dZ without copying. */
+void or_gemm(int64_t M, int64_t N, int64_t K,
+             const double *A, int64_t a_rs, int64_t a_cs,
+             const double *B, int64_t b_rs, int64_t b_cs,
+             double *C)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i) {
+        for (int64_t j = 0; j < N; ++j) {
+            double acc = 0.0;
+            for (int64_t k = 0; k < K; ++k)
+                acc += A[i * a_rs + k * a_cs] * B[k * b_rs + j * b_cs];
+            C[i * N + j] = acc;
+        }
+    }
+}
+
+/* ---------------------------------------------------------------------- */
+/* element-wise activations                                                */
+/* ---------------------------------------------------------------------- */
+enum { OR_RELU = 0, OR_GELU = 1, OR_SILU = 2 };
+
+static double act_f(int kind, double z)
+{
+    switch (kind) {
+    case OR_RELU: return z > 0.0 ? z : 0.0;
+    /* GeLU, exact form: z * Phi(z), Phi the standard normal CDF */
+    case OR_GELU: return 0.5 * z * (1.0 + erf(z / sqrt(2.0)));
+    /* SiLU (swish with beta = 1): z * sigmoid(z) */
+    case OR_SILU: return z / (1.0 + exp(-z));
+    }
+    return NAN;
+}
+
+static double act_df(int kind, double z)
+{
+    switch (kind) {
+    /* derivative 0 wherever the pre-activation is not positive (z = 0 included) */
+    case OR_RELU: return z > 0.0 ? 1.0 : 0.0;
+    case OR_GELU: {
+        double Phi = 0.5 * (1.0 + erf(z / sqrt(2.0)));
+        double phi = exp(-0.5 * z * z) / sqrt(2.0 * M_PI);
+        return Phi + z * phi;
+    }
+    case OR_SILU: {
+        double sg = 1.0 / (1.0 + exp(-z));
+        return sg * (1.0 + z * (1.0 - sg));
+    }
+    }
+    return NAN;
+}
+
+void or_act(int kind, int64_t n, const double *z, double *out)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = act_f(kind, z[i]);
+}
+
+void or_act_grad(int kind, int64_t n, const double *z, double *out)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = act_df(kind, z[i]);
+}
+
+/* ---------------------------------------------------------------------- */
+/* vocab-parallel cross entropy, one shard's statistics                    */
+/* ---------------------------------------------------------------------- */
+
+/* For every position r of the [s, Vs] logit slice held by the shard that
+ * owns global vocab rows [start, start+Vs):
+ *   m[r]  = max_j z[r,j]                       (-inf when Vs = 0)
+ *   se[r] = sum_j exp(z[r,j] - m[r])           (0 when Vs = 0)
+ *   tl[r] = z[r, y_r - start] if start <= y_r < start+Vs, else 0.
+ * The sum of exponentials is taken against the shard's own maximum; the
+ * combine below rescales it by exp(m_i - M) to the global maximum M. */
+void or_ce_stats(int64_t s, int64_t Vs, int64_t start,
+                 const double *z, const int64_t *target,
+                 double *m, double *se, double *tl)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < s; ++r) {
+        const double *row = z + r * Vs;
+        double mx = -INFINITY;
+        for (int64_t j = 0; j < Vs; ++j)
+            if (row[j] > mx) mx = row[j];
+        double acc = 0.0;
+        for (int64_t j = 0; j < Vs; ++j)
+            acc += exp(row[j] - mx);
+        int64_t y = target[r];
+        m[r] = mx;
+        se[r] = acc;
+        tl[r] = (y >= start && y < start + Vs) ? row[y - start] : 0.0;
+    }
+}
+
+/* Combine the t shards' statistics into the per-position loss
+ *   M = max_i m_i,  S = sum_i se_i * exp(m_i - M),  loss = M + ln S - sum_i tl_i.
+ * Arrays are [t, s] row-major. */
+void or_ce_combine(int64_t t, int64_t s, const double *m, const double *se,
+                   const double *tl, double *loss)
+{
+    for (int64_t r = 0; r < s; ++r) {
+        double M = -INFINITY;
+        for (int64_t i = 0; i < t; ++i)
+            if (m[i * s + r] > M) M = m[i * s + r];
+        double S = 0.0, T = 0.0;
+        for (int64_t i = 0; i < t; ++i) {
+            if (se[i * s + r] > 0.0) S += se[i * s + r] * exp(m[i * s + r] - M);
+            T += tl[i * s + r];
+        }
+        loss[r] = M + log(S) - T;
+    }
+}
+
+/* The unsharded definition: loss_r = logsumexp_j z[r,j] - z[r, y_r] over the
+ * whole vocabulary [s, V]. */
+void or_ce_direct(int64_t s, int64_t V, const double *z, const int64_t *target,
+                  double *loss)
+{
+    for (int64_t r = 0; r < s; ++r) {
+        const double *row = z + r * V;
+        double mx = -INFINITY;
+        for (int64_t j = 0; j < V; ++j)
+            if (row[j] > mx) mx = row[j];
+        double acc = 0.0;
+        for (int64_t j = 0; j < V; ++j) acc += exp(row[j] - mx);
+        loss[r] = mx + log(acc) - row[target[r]];
+    }
+}
+
+/* ---------------------------------------------------------------------- */
+/* vocab-sharded embedding lookup                                          */
+/* ---------------------------------------------------------------------- */
+
+/* out[r,:] = table[id_r - start, :] when start <= id_r < start+Vs, else the
+ * zero vector.  The rows are copied as raw 16-bit patterns (bfloat16 or any
+ * other 2-byte type): a lookup moves bits, it does no arithmetic. */
+void or_embed_u16(int64_t n, int64_t Vs, int64_t h, int64_t start,
+                  const int64_t *ids, const uint16_t *table, uint16_t *out)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+        int64_t id = ids[r];
+        int in = (id >= start && id < start + Vs);
+        for (int64_t c = 0; c < h; ++c)
+            out[r * h + c] = in ? table[(id - start) * h + c] : (uint16_t)0;
+    }
+}
+
+/* the same with 4-byte elements (fp32 tables) */
+void or_embed_u32(int64_t n, int64_t Vs, int64_t h, int64_t start,
+                  const int64_t *ids, const uint32_t *table, uint32_t *out)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+        int64_t id = ids[r];
+        int in = (id >= start && id < start + Vs);
+        for (int64_t c = 0; c < h; ++c)
+            out[r * h + c] = in ? table[(id - start) * h + c] : 0u;
+    }
+}
+
+int or_version(void) { return 1; }
