@@ -1,0 +1,209 @@
+/*
+ * tpshard.h -- C ABI of libtpshard: one GPU's shard of a Megatron-style
+ * tensor-parallel transformer layer, for AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow two public pages:
+ *   [book]  "7.3 模型并行与张量并行：把一层切到多张卡上" (LLM internals book):
+ *           §7.3.2 column and row splits with the two-card worked example,
+ *           §7.3.3 the backward pass and the f / g operators,
+ *           §7.3.4 attention by heads, SwiGLU, embedding and LM head by vocab;
+ *   [lec16] CMU 11-868 lecture 16 notes, §5 "张量并行": §5.2 the MLP (column
+ *           then row), §5.3 attention by heads, §5.5 vocab-parallel embedding
+ *           and fused cross entropy.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Matrices are dense, row-major and contiguous.  Weights are stored
+ *    [in, out] as the pages write them (Y = X.W), not [out, in].
+ *  - Shard i of t holds columns [i*f/t, (i+1)*f/t) of a column-split weight and
+ *    the same rows of the row-split weight that follows it ([book] §7.3.2: card
+ *    0 holds the first columns of W1 and the first rows of W2).  The calls work
+ *    on one shard; the caller passes that shard's slices and sizes.
+ *  - Pointers X, W*, Z, ... are DEVICE pointers owned by the caller.  The
+ *    library allocates no memory, frees nothing and keeps no state between
+ *    calls.  Every pointer must be 16-byte aligned (TP_EALIGN otherwise).
+ *    Outputs are overwritten (never accumulated into) and must not alias any
+ *    input or each other.  Inputs are never modified.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *    enqueue work and return; results are valid once the caller synchronizes
+ *    the stream.  Calls on different streams may run concurrently when their
+ *    outputs and workspaces are distinct.
+ *  - Every argument is checked before anything is enqueued: on an error no
+ *    kernel runs, the call returns the status and tp_last_error() (per host
+ *    thread) says which check failed.  A failed launch returns TP_EHIP.
+ *    Faults inside a kernel surface at the caller's synchronization.
+ *  - Sizes are int64_t.  Negative sizes are TP_ESHAPE.  A zero size is legal:
+ *    outputs with no elements are not touched, and outputs of an empty
+ *    contraction (zero inner size) are written as the activation of zero.
+ *    Each size must be below 2^31.
+ *  - dtype TP_DT_BF16: bfloat16 storage of every tensor (inputs, outputs,
+ *    saved activations, gradients), fp32 accumulation, round-to-nearest-even
+ *    on every store.  TP_DT_F32: fp32 storage and arithmetic throughout.
+ *  - Thread safety: the library holds no shared mutable state except the
+ *    per-thread last-error string.
+ */
+#ifndef TPSHARD_H
+#define TPSHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TP_ABI_VERSION 1
+
+typedef enum {
+    TP_OK = 0,
+    TP_EINVAL = 1,        /* NULL pointer or bad enum value */
+    TP_ESHAPE = 2,        /* negative size, size >= 2^31, or inconsistent sizes */
+    TP_EDTYPE = 3,        /* dtype not valid for this call */
+    TP_EALIGN = 4,        /* a pointer is not 16-byte aligned */
+    TP_EWORKSPACE = 5,    /* workspace missing or smaller than the size query */
+    TP_EHIP = 6,          /* the HIP runtime reported an error at launch */
+    TP_EUNSUPPORTED = 7   /* valid request this build does not implement */
+} tp_status;
+
+typedef enum { TP_DT_F32 = 0, TP_DT_BF16 = 1 } tp_dtype;
+
+/* Element-wise activation of the MLP shard.  GELU is the exact form
+ * z * Phi(z) with Phi the standard normal CDF (the pages name GeLU without a
+ * formula).  ReLU's derivative is taken as 0 at z = 0. */
+typedef enum { TP_ACT_RELU = 0, TP_ACT_GELU = 1 } tp_act;
+
+/* ------------------------------------------------------------------------ */
+/* MLP shard: column-parallel GEMM + activation, row-parallel GEMM          */
+/* ------------------------------------------------------------------------ */
+
+/* Forward of the MLP shard ([lec16] §5.2; [book] §7.3.2):
+ *     Z = X . W1(i)        X [s,h], W1(i) [h,ft]        -> Z [s,ft]
+ *     H = act(Z)                                         -> H [s,ft]
+ *     Y(i) = H . W2(i)     W2(i) [ft,h]                  -> Y [s,h]
+ * Y(i) is this shard's partial sum: the g operator's all-reduce over the t
+ * shards gives the layer output.  Z may be NULL when act is TP_ACT_RELU (the
+ * backward then takes the mask from H > 0); it is required for GELU.
+ * dt: TP_DT_F32 or TP_DT_BF16 for every tensor. */
+int tp_mlp_fwd(int act, int dt, int64_t s, int64_t h, int64_t ft,
+               const void *X, const void *W1, const void *W2,
+               void *Z, void *H, void *Y, void *stream);
+
+/* Bytes of device workspace tp_mlp_bwd needs for these sizes (0 on bad input). */
+size_t tp_mlp_bwd_workspace(int dt, int64_t s, int64_t h, int64_t ft);
+
+/* Backward of the MLP shard ([book] §7.3.3):
+ *     dH = dY . W2(i)^T;  dZ = dH * act'(Z)   (ReLU: dZ = dH where Z > 0, else 0)
+ *     dX(i) = dZ . W1(i)^T                     -> dX [s,h]: the partial sum the
+ *                                                 f operator's all-reduce adds
+ *     dW1(i) = X^T . dZ                        -> dW1 [h,ft]
+ *     dW2(i) = H^T . dY                        -> dW2 [ft,h]
+ * Z and H are the forward's outputs for the same X, W1 (Z may be NULL for
+ * ReLU, then the mask is H > 0).  dY [s,h] is the full output gradient
+ * (g's backward is the identity).  ws / ws_bytes: device workspace of at least
+ * tp_mlp_bwd_workspace() bytes, 256-byte aligned; its contents on entry do not
+ * matter and are garbage on return. */
+int tp_mlp_bwd(int act, int dt, int64_t s, int64_t h, int64_t ft,
+               const void *X, const void *W1, const void *W2,
+               const void *Z, const void *H, const void *dY,
+               void *dX, void *dW1, void *dW2,
+               void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* SwiGLU shard ([book] §7.3.4: gate and up split by columns, product on the */
+/* shard, down split by rows).  Reading: A = SiLU(X.Wg) * (X.Wu), swish beta 1.*/
+/* ------------------------------------------------------------------------ */
+
+/* Forward:  G = X.Wg(i), U = X.Wu(i)  (Wg, Wu [h,ft])   -> G, U [s,ft]
+ *           A = SiLU(G) * U                              -> A [s,ft]
+ *           Y(i) = A . Wd(i)           (Wd [ft,h])       -> Y [s,h] partial sum
+ * G, U and A are saved for the backward.  dt: TP_DT_BF16 or TP_DT_F32. */
+int tp_swiglu_fwd(int dt, int64_t s, int64_t h, int64_t ft,
+                  const void *X, const void *Wg, const void *Wu, const void *Wd,
+                  void *G, void *U, void *A, void *Y, void *stream);
+
+size_t tp_swiglu_bwd_workspace(int dt, int64_t s, int64_t h, int64_t ft);
+
+/* Backward:  dA = dY . Wd^T;  dG = dA * U * SiLU'(G);  dU = dA * SiLU(G)
+ *            dWd = A^T . dY                              -> [ft,h]
+ *            dX(i) = dG . Wg^T + dU . Wu^T               -> [s,h] partial sum
+ *            dWg = X^T . dG,  dWu = X^T . dU             -> [h,ft] each
+ * G, U, A are the forward's outputs.  Workspace as for tp_mlp_bwd. */
+int tp_swiglu_bwd(int dt, int64_t s, int64_t h, int64_t ft,
+                  const void *X, const void *Wg, const void *Wu, const void *Wd,
+                  const void *G, const void *U, const void *A, const void *dY,
+                  void *dX, void *dWg, void *dWu, void *dWd,
+                  void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Attention projections split by heads ([book] §7.3.4; [lec16] §5.3):       */
+/* Q/K/V column-split (whole heads per shard), W_O row-split.  The attention  */
+/* core between them is not part of these calls.                             */
+/* ------------------------------------------------------------------------ */
+
+/* Forward:  Q = X.Wq(i) [s,dq];  K = X.Wk(i) [s,dkv];  V = X.Wv(i) [s,dkv]
+ *           Y(i) = O . Wo(i)      O [s,dq] (the core's output), Wo [dq,h]
+ * Wq [h,dq], Wk and Wv [h,dkv].  Y is this shard's partial sum. */
+int tp_attn_proj_fwd(int dt, int64_t s, int64_t h, int64_t dq, int64_t dkv,
+                     const void *X, const void *Wq, const void *Wk, const void *Wv,
+                     const void *O, const void *Wo,
+                     void *Q, void *K, void *V, void *Y, void *stream);
+
+size_t tp_attn_proj_bwd_workspace(int dt, int64_t s, int64_t h, int64_t dq, int64_t dkv);
+
+/* Backward:  dX(i) = dQ.Wq^T + dK.Wk^T + dV.Wv^T   -> [s,h] partial sum (f's input)
+ *            dWq = X^T.dQ, dWk = X^T.dK, dWv = X^T.dV
+ *            dO = dY . Wo^T  [s,dq];  dWo = O^T . dY  [dq,h]
+ * dQ, dK, dV are the gradients the attention core hands back; dY [s,h]. */
+int tp_attn_proj_bwd(int dt, int64_t s, int64_t h, int64_t dq, int64_t dkv,
+                     const void *X, const void *Wq, const void *Wk, const void *Wv,
+                     const void *O, const void *Wo,
+                     const void *dQ, const void *dK, const void *dV, const void *dY,
+                     void *dX, void *dWq, void *dWk, void *dWv, void *dO, void *dWo,
+                     void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Vocab-parallel output layer, cross entropy and embedding                   */
+/* ([book] §7.3.4; [lec16] §5.5)                                              */
+/* ------------------------------------------------------------------------ */
+
+/* LM head split by vocab: logits(i) = Hf . Wlm(i), Hf [s,h], Wlm(i) [h,Vs],
+ * logits [s,Vs] always fp32.  dt is the storage type of Hf and Wlm. */
+int tp_lm_head_fwd(int dt, int64_t s, int64_t h, int64_t Vs,
+                   const void *Hf, const void *Wlm, float *logits, void *stream);
+
+/* The shard's cross-entropy statistics for every position r of its fp32
+ * logit slice z [s,Vs], which covers global vocab ids [vocab_start,
+ * vocab_start+Vs):
+ *     lmax[r]    = max_j z[r,j]                       (-inf if Vs == 0)
+ *     lsumexp[r] = sum_j exp(z[r,j] - lmax[r])        (0 if Vs == 0)
+ *     tlogit[r]  = z[r, target[r]-vocab_start] if the target lies in the
+ *                  shard, else 0.0
+ * target [s] holds global int64 ids; any id outside the shard (negative or
+ * beyond the vocabulary included) just gives tlogit = 0.  Combining the t
+ * shards, M = max m_i, S = sum se_i exp(m_i - M), gives
+ * loss = M + ln S - sum tlogit_i, three scalars per token exchanged instead of
+ * the logits.  The sum of exponentials is taken against the shard's own max
+ * (one pass); the combine rescales it.  vocab_start >= 0. */
+int tp_vocab_ce(int64_t s, int64_t Vs, int64_t vocab_start,
+                const float *logits, const int64_t *target,
+                float *lmax, float *lsumexp, float *tlogit, void *stream);
+
+/* Embedding rows of a vocab shard: out[r,:] = table[ids[r]-vocab_start, :]
+ * when vocab_start <= ids[r] < vocab_start+Vs, else the zero vector (all bits
+ * 0).  table [Vs,h], out [n,h]; dt is the element type (rows are copied bit
+ * for bit).  Summing the t shards' outputs (the all-reduce) gives the full
+ * lookup, since exactly one shard owns each valid id. */
+int tp_vocab_embed(int dt, int64_t n, int64_t Vs, int64_t h, int64_t vocab_start,
+                   const int64_t *ids, const void *table, void *out, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Diagnostics                                                               */
+/* ------------------------------------------------------------------------ */
+const char *tp_status_string(int status);   /* static string; never NULL */
+const char *tp_last_error(void);            /* detail of this thread's last error */
+int tp_abi_version(void);                   /* TP_ABI_VERSION */
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TPSHARD_H */

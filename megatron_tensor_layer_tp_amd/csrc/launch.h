@@ -1,0 +1,26 @@
+// launch.h -- internal launchers of libtpshard (not part of the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "gemm_desc.h"
+
+enum GemmLayout : int {
+  GEMM_NN = 0,  // A [M][K], B [K][N]
+  GEMM_NT = 1,  // A [M][K], B [N][K]
+  GEMM_TN = 2,  // A [K][M], B [K][N]
+};
+
+// bf16 MFMA tiles: bm, bn in {128, 256}; vec = 16-byte loads are legal for
+// every operand (aligned pointers, leading dimensions and extents multiple of 8).
+hipError_t tp_launch_gemm_bf16(const GemmDesc &d, int layout, int epi, bool out_f32, int bm, int bn,
+                               bool vec, hipStream_t st);
+hipError_t tp_launch_splitk_reduce(const GemmDesc &d, bool out_f32, hipStream_t st);
+
+// fp32 storage and arithmetic (64x64 tiles, any layout, any extents).
+constexpr int TP_F32_TILE = 64;
+hipError_t tp_launch_gemm_f32(const GemmDesc &d, int layout, int epi, hipStream_t st);
+
+hipError_t tp_launch_vocab_ce(int64_t s, int64_t Vs, int64_t start, const float *z, const int64_t *tgt,
+                              float *m, float *se, float *tl, hipStream_t st);
+hipError_t tp_launch_vocab_embed(int elem_bytes, int64_t n, int64_t Vs, int64_t h, int64_t start,
+                                 const int64_t *ids, const void *table, void *out, hipStream_t st);

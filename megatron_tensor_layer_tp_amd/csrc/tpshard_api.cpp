@@ -1,0 +1,811 @@
+// tpshard_api.cpp -- the extern "C" entry points of libtpshard.
+//
+// Each call validates every argument before anything is enqueued, plans the
+// launch (tile shape, split-K) from the sizes alone -- so the workspace size
+// queries and the calls agree -- and enqueues its kernels on the caller's
+// stream.  No allocation, no state beyond the per-thread error string.
+//
+// The operations are those of the pages: column- and row-parallel products
+// and the two-card worked example (book "7.3 模型并行与张量并行" §7.3.2),
+// the backward pass (§7.3.3), attention/SwiGLU/vocab sharding (§7.3.4), and
+// the fused vocab-parallel cross entropy (lecture 16 notes §5.5).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/tpshard.h"
+#include "gemm_desc.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = std::string(tp_status_string(code)) + ": " + buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return TP_OK;
+}
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+constexpr int kCUs = 256;     // MI355X compute units
+constexpr int kBK = 64;       // K tile of both GEMM paths
+
+// ---------------------------------------------------------------- checks
+struct Checker {
+  int status = TP_OK;
+  bool dim(int64_t v, const char *name) {
+    if (status) return false;
+    if (v < 0 || v > kMaxDim) {
+      status = fail(TP_ESHAPE, "%s = %lld is negative or >= 2^31", name, (long long)v);
+      return false;
+    }
+    return true;
+  }
+  // a pointer may be NULL only when its tensor has no elements
+  bool ptr(const void *p, int64_t nelem, const char *name) {
+    if (status) return false;
+    if (nelem > 0 && p == nullptr) {
+      status = fail(TP_EINVAL, "%s is NULL", name);
+      return false;
+    }
+    if (((uintptr_t)p & 15) != 0) {
+      status = fail(TP_EALIGN, "%s = %p is not 16-byte aligned", name, p);
+      return false;
+    }
+    return true;
+  }
+  bool dtype(int dt, bool f32_ok, const char *call) {
+    if (status) return false;
+    if (dt != TP_DT_F32 && dt != TP_DT_BF16) {
+      status = fail(TP_EINVAL, "%s: dtype %d is not a tp_dtype", call, dt);
+      return false;
+    }
+    if (dt == TP_DT_F32 && !f32_ok) {
+      status = fail(TP_EUNSUPPORTED, "%s: fp32 storage is not supported", call);
+      return false;
+    }
+    return true;
+  }
+  bool act(int a) {
+    if (status) return false;
+    if (a != TP_ACT_RELU && a != TP_ACT_GELU) {
+      status = fail(TP_EINVAL, "act %d is not a tp_act", a);
+      return false;
+    }
+    return true;
+  }
+  bool elems(int64_t a, int64_t b, int64_t &out, const char *what) {
+    if (status) return false;
+    if (a != 0 && b > INT64_MAX / 8 / a) {
+      status = fail(TP_ESHAPE, "%s has too many elements", what);
+      return false;
+    }
+    out = a * b;
+    return true;
+  }
+};
+
+// ---------------------------------------------------------------- planning
+struct Plan {
+  int bm = 128, bn = 128, splits = 1, kt_per_split = 1, tiles_m = 0, tiles_n = 0;
+  bool vec = true;
+  size_t ws_bytes = 0;  // split-K partials
+};
+
+struct Spec {               // one product, described before planning
+  int layout = GEMM_NN;
+  int epi = EPI_STORE;
+  bool out_f32 = false;
+  int64_t M = 0, K = 0;     // K = total when kseg
+  int nseg = 1;
+  bool kseg = false;
+  bool dual = false;
+  bool can_split = false;   // a workspace for split-K partials is available
+  int64_t seg[TP_MAX_SEG] = {0, 0, 0};  // N-extents (N-segments) or K-extents (K-segments)
+  int64_t N = 0;            // total N (kseg or single segment)
+  int64_t lds[12] = {};     // every leading dimension involved
+  int nlds = 0;
+  void ld(int64_t v) { lds[nlds++] = v; }
+};
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int64_t ntiles_n(const Spec &s, int bn) {
+  if (s.kseg) return cdiv(s.N, bn);
+  const int w = s.dual ? bn / 2 : bn;
+  int64_t t = 0;
+  for (int i = 0; i < s.nseg; ++i) t += cdiv(s.seg[i], w);
+  return t;
+}
+
+int64_t ktiles(const Spec &s) {
+  if (!s.kseg) return cdiv(s.K, kBK);
+  int64_t t = 0;
+  for (int i = 0; i < s.nseg; ++i) t += cdiv(s.seg[i], kBK);
+  return t;
+}
+
+// Relative MFMA efficiency of each tile shape (larger tiles re-read less and
+// keep the LDS traffic per MFMA lower); 128x128 runs two workgroups per CU.
+double tile_eff(int bm, int bn) {
+  if (bm == 256 && bn == 256) return 1.0;
+  if (bm == 128 && bn == 128) return 0.72;
+  return 0.85;
+}
+
+Plan plan_bf16(const Spec &s) {
+  Plan p;
+  bool vec = true;
+  for (int i = 0; i < s.nlds; ++i) vec &= s.lds[i] % 8 == 0;
+  vec &= s.M % 8 == 0;
+  if (s.kseg) {
+    vec &= s.N % 8 == 0;
+    for (int i = 0; i < s.nseg; ++i) vec &= s.seg[i] % 8 == 0;
+  } else {
+    vec &= s.K % 8 == 0;
+    for (int i = 0; i < s.nseg; ++i) vec &= s.seg[i] % 8 == 0;
+  }
+  p.vec = vec;
+  const int64_t KT = ktiles(s);
+  const bool can_split = s.can_split && s.epi == EPI_STORE && !s.dual && KT >= 8;
+  static const int shapes[4][2] = {{256, 256}, {256, 128}, {128, 256}, {128, 128}};
+  double best = 1e300;
+  for (auto &sh : shapes) {
+    const int bm = sh[0], bn = sh[1];
+    if (!vec && !(bm == 128 && bn == 128)) continue;
+    const int64_t tm = cdiv(s.M, bm), tn = ntiles_n(s, bn);
+    const int64_t tiles = tm * tn;
+    const int slots = (bm == 128 && bn == 128) ? 2 * kCUs : kCUs;
+    const double per_slot_rate = tile_eff(bm, bn) * ((bm == 128 && bn == 128) ? 0.5 : 1.0);
+    for (int sp = 1; sp <= (can_split ? 8 : 1); ++sp) {
+      if (sp > 1 && (KT / sp < 4 || tiles * (sp - 1) >= slots)) break;
+      const int64_t kps = cdiv(std::max<int64_t>(KT, 1), sp);
+      const int64_t nblk = tiles * sp;
+      const double waves = (double)cdiv(nblk, slots);
+      // time in units of one 128x128x64 MFMA step on a full CU
+      double t = waves * kps * (bm * bn) / (128.0 * 128.0) / per_slot_rate;
+      if (sp > 1) {
+        // partial writes + the reduction pass, ~1 MFMA step per 4 KB of fp32 traffic
+        const double bytes = (double)s.M * s.N * 4.0 * (2.0 * sp + 1.0);
+        t += bytes / kCUs / 4096.0 + 4.0;
+      }
+      if (t < best * 0.999) {
+        best = t;
+        p.bm = bm;
+        p.bn = bn;
+        p.splits = sp;
+        p.kt_per_split = (int)kps;
+        p.tiles_m = (int)tm;
+        p.tiles_n = (int)tn;
+      }
+    }
+  }
+  if (p.splits > 1) p.ws_bytes = (size_t)p.splits * s.M * s.N * sizeof(float);
+  return p;
+}
+
+Plan plan_f32(const Spec &s) {
+  Plan p;
+  p.bm = p.bn = TP_F32_TILE;
+  p.tiles_m = (int)cdiv(s.M, TP_F32_TILE);
+  int64_t tn = 0;
+  if (s.kseg) tn = cdiv(s.N, TP_F32_TILE);
+  else
+    for (int i = 0; i < s.nseg; ++i) tn += cdiv(s.seg[i], TP_F32_TILE);
+  p.tiles_n = (int)tn;
+  p.splits = 1;
+  p.kt_per_split = (int)std::max<int64_t>(ktiles(s), 1);
+  return p;
+}
+
+Plan plan(const Spec &s, int dt) { return dt == TP_DT_BF16 ? plan_bf16(s) : plan_f32(s); }
+
+size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+// Build the kernel descriptor for a spec + plan and launch it (plus the
+// split-K reduction).  Pointers: A[i], B[i], C[i] per segment.
+struct Ptrs {
+  const void *A[TP_MAX_SEG] = {};
+  int64_t lda[TP_MAX_SEG] = {};
+  const void *B[TP_MAX_SEG] = {};
+  int64_t ldb[TP_MAX_SEG] = {};
+  void *C[TP_MAX_SEG] = {};
+  int64_t ldc[TP_MAX_SEG] = {};
+  const void *ai0 = nullptr, *ai1 = nullptr;
+  int64_t ldai = 0;
+  void *ao0 = nullptr, *ao1 = nullptr;
+  int64_t ldao = 0;
+  int act = ACT_RELU;
+};
+
+int run(const Spec &s, const Ptrs &q, int dt, void *ws, hipStream_t st, const char *what) {
+  const Plan p = plan(s, dt);
+  GemmDesc d;
+  std::memset(&d, 0, sizeof d);
+  d.M = (int32_t)s.M;
+  d.K = (int32_t)s.K;
+  d.nseg = s.nseg;
+  d.kseg = s.kseg;
+  d.dual = s.dual;
+  d.act = q.act;
+  int64_t col = 0, tile = 0;
+  const int wn = (s.dual && dt == TP_DT_BF16) ? p.bn / 2 : p.bn;
+  for (int i = 0; i < s.nseg; ++i) {
+    d.seg_len[i] = (int32_t)s.seg[i];
+    d.seg_col0[i] = (int32_t)col;
+    d.seg_tile0[i] = (int32_t)tile;
+    col += s.seg[i];
+    tile += s.kseg ? cdiv(s.seg[i], kBK) : cdiv(s.seg[i], wn);
+  }
+  d.seg_tile0[s.nseg] = (int32_t)tile;
+  d.N = (int32_t)(s.kseg ? s.N : (s.dual ? s.seg[0] : col));
+  for (int i = 0; i < TP_MAX_SEG; ++i) {
+    d.A[i] = q.A[i];
+    d.lda[i] = q.lda[i];
+    d.B[i] = q.B[i];
+    d.ldb[i] = q.ldb[i];
+    d.C[i] = q.C[i];
+    d.ldc[i] = q.ldc[i];
+  }
+  d.ai0 = q.ai0;
+  d.ai1 = q.ai1;
+  d.ldai = q.ldai;
+  d.ao0 = q.ao0;
+  d.ao1 = q.ao1;
+  d.ldao = q.ldao;
+  d.splits = p.splits;
+  d.kt_per_split = p.kt_per_split;
+  d.tiles_m = p.tiles_m;
+  d.tiles_n = p.tiles_n;
+  d.group_m = 8;
+  d.ws = (float *)ws;
+  if (p.splits > 1 && ws == nullptr) return fail(TP_EWORKSPACE, "%s: split-K plan without workspace", what);
+  hipError_t e;
+  if (dt == TP_DT_F32) {
+    e = tp_launch_gemm_f32(d, s.layout, s.epi, st);
+  } else if (p.splits > 1) {
+    e = tp_launch_gemm_bf16(d, s.layout, EPI_PARTIAL, true, p.bm, p.bn, p.vec, st);
+    if (e == hipSuccess) e = tp_launch_splitk_reduce(d, s.out_f32, st);
+  } else {
+    e = tp_launch_gemm_bf16(d, s.layout, s.epi, s.out_f32, p.bm, p.bn, p.vec, st);
+  }
+  if (e != hipSuccess) return fail(TP_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return TP_OK;
+}
+
+size_t esize(int dt) { return dt == TP_DT_F32 ? 4 : 2; }
+
+// ---------------------------------------------------------------- specs
+// MLP (all sizes already validated)
+Spec spec_nn(int64_t M, int64_t N, int64_t K, int epi) {
+  Spec s;
+  s.layout = GEMM_NN;
+  s.epi = epi;
+  s.M = M;
+  s.K = K;
+  s.N = N;
+  s.seg[0] = N;
+  s.ld(K);   // A [M][K]
+  s.ld(N);   // B [K][N], C [M][N]
+  return s;
+}
+Spec spec_nt(int64_t M, int64_t N, int64_t K, int epi) {
+  Spec s = spec_nn(M, N, K, epi);
+  s.layout = GEMM_NT;
+  return s;
+}
+Spec spec_tn(int64_t M, int64_t N, int64_t K) {
+  Spec s;
+  s.layout = GEMM_TN;
+  s.epi = EPI_STORE;
+  s.M = M;
+  s.K = K;
+  s.N = N;
+  s.seg[0] = N;
+  s.ld(M);   // A [K][M]
+  s.ld(N);   // B [K][N], C [M][N]
+  return s;
+}
+
+// tp_mlp_bwd workspace: dZ [s,ft] then the split-K partials of dW1 / dW2
+struct MlpBwdLayout {
+  Spec g_dz, g_dw2, g_dx, g_dw1;
+  size_t dz_bytes = 0, part_bytes = 0, total = 0;
+};
+MlpBwdLayout mlp_bwd_layout(int dt, int64_t s, int64_t h, int64_t ft) {
+  MlpBwdLayout L;
+  L.g_dz = spec_nt(s, ft, h, EPI_ACT_BWD);
+  L.g_dz.ld(h);
+  L.g_dw2 = spec_tn(ft, h, s);
+  L.g_dx = spec_nt(s, h, ft, EPI_STORE);
+  L.g_dw1 = spec_tn(h, ft, s);
+  for (Spec *g : {&L.g_dz, &L.g_dw2, &L.g_dx, &L.g_dw1}) g->can_split = true;
+  L.dz_bytes = align256((size_t)s * ft * esize(dt));
+  for (const Spec *g : {&L.g_dz, &L.g_dw2, &L.g_dx, &L.g_dw1})
+    L.part_bytes = std::max(L.part_bytes, align256(plan(*g, dt).ws_bytes));
+  L.total = L.dz_bytes + L.part_bytes;
+  return L;
+}
+
+struct SwigluBwdLayout {
+  Spec g_da, g_dwd, g_dx, g_dwgu;
+  size_t dg_bytes = 0, part_bytes = 0, total = 0;
+};
+SwigluBwdLayout swiglu_bwd_layout(int dt, int64_t s, int64_t h, int64_t ft) {
+  SwigluBwdLayout L;
+  L.g_da = spec_nt(s, ft, h, EPI_SWIGLU_BWD);
+  L.g_dwd = spec_tn(ft, h, s);
+  // dX = dG.Wg^T + dU.Wu^T: two K-segments of width ft
+  Spec dx;
+  dx.layout = GEMM_NT;
+  dx.epi = EPI_STORE;
+  dx.M = s;
+  dx.N = h;
+  dx.K = 2 * ft;
+  dx.nseg = 2;
+  dx.kseg = true;
+  dx.seg[0] = dx.seg[1] = ft;
+  dx.ld(ft);
+  dx.ld(h);
+  L.g_dx = dx;
+  // [dWg | dWu] = X^T . [dG | dU]: two N-segments of width ft
+  Spec dw;
+  dw.layout = GEMM_TN;
+  dw.epi = EPI_STORE;
+  dw.M = h;
+  dw.K = s;
+  dw.nseg = 2;
+  dw.seg[0] = dw.seg[1] = ft;
+  dw.N = 2 * ft;
+  dw.ld(h);
+  dw.ld(ft);
+  L.g_dwgu = dw;
+  for (Spec *g : {&L.g_da, &L.g_dwd, &L.g_dx, &L.g_dwgu}) g->can_split = true;
+  L.dg_bytes = align256((size_t)s * ft * esize(dt));
+  for (const Spec *g : {&L.g_da, &L.g_dwd, &L.g_dx, &L.g_dwgu})
+    L.part_bytes = std::max(L.part_bytes, align256(plan(*g, dt).ws_bytes));
+  L.total = 2 * L.dg_bytes + L.part_bytes;
+  return L;
+}
+
+struct AttnBwdLayout {
+  Spec g_dx, g_dwqkv, g_do, g_dwo;
+  size_t part_bytes = 0, total = 0;
+};
+AttnBwdLayout attn_bwd_layout(int dt, int64_t s, int64_t h, int64_t dq, int64_t dkv) {
+  AttnBwdLayout L;
+  Spec dx;
+  dx.layout = GEMM_NT;
+  dx.epi = EPI_STORE;
+  dx.M = s;
+  dx.N = h;
+  dx.K = dq + 2 * dkv;
+  dx.nseg = 3;
+  dx.kseg = true;
+  dx.seg[0] = dq;
+  dx.seg[1] = dx.seg[2] = dkv;
+  dx.ld(dq);
+  dx.ld(dkv);
+  dx.ld(h);
+  L.g_dx = dx;
+  Spec dw;
+  dw.layout = GEMM_TN;
+  dw.epi = EPI_STORE;
+  dw.M = h;
+  dw.K = s;
+  dw.nseg = 3;
+  dw.seg[0] = dq;
+  dw.seg[1] = dw.seg[2] = dkv;
+  dw.N = dq + 2 * dkv;
+  dw.ld(h);
+  dw.ld(dq);
+  dw.ld(dkv);
+  L.g_dwqkv = dw;
+  L.g_do = spec_nt(s, dq, h, EPI_STORE);
+  L.g_dwo = spec_tn(dq, h, s);
+  for (Spec *g : {&L.g_dx, &L.g_dwqkv, &L.g_do, &L.g_dwo}) g->can_split = true;
+  for (const Spec *g : {&L.g_dx, &L.g_dwqkv, &L.g_do, &L.g_dwo})
+    L.part_bytes = std::max(L.part_bytes, align256(plan(*g, dt).ws_bytes));
+  L.total = L.part_bytes;
+  return L;
+}
+
+bool ws_ok(Checker &c, const void *ws, size_t have, size_t need, const char *call) {
+  if (c.status) return false;
+  if (need == 0) return true;
+  if (ws == nullptr || have < need) {
+    c.status = fail(TP_EWORKSPACE, "%s needs %zu workspace bytes, got %zu (%p)", call, need, have, ws);
+    return false;
+  }
+  if (((uintptr_t)ws & 255) != 0) {
+    c.status = fail(TP_EALIGN, "%s: workspace %p is not 256-byte aligned", call, ws);
+    return false;
+  }
+  return true;
+}
+
+}  // namespace
+
+// ====================================================================== ABI
+extern "C" {
+
+const char *tp_status_string(int status) {
+  switch (status) {
+  case TP_OK: return "TP_OK";
+  case TP_EINVAL: return "TP_EINVAL";
+  case TP_ESHAPE: return "TP_ESHAPE";
+  case TP_EDTYPE: return "TP_EDTYPE";
+  case TP_EALIGN: return "TP_EALIGN";
+  case TP_EWORKSPACE: return "TP_EWORKSPACE";
+  case TP_EHIP: return "TP_EHIP";
+  case TP_EUNSUPPORTED: return "TP_EUNSUPPORTED";
+  }
+  return "TP_UNKNOWN_STATUS";
+}
+
+const char *tp_last_error(void) { return g_last_error.c_str(); }
+
+int tp_abi_version(void) { return TP_ABI_VERSION; }
+
+// ------------------------------------------------------------------ MLP
+int tp_mlp_fwd(int act, int dt, int64_t s, int64_t h, int64_t ft, const void *X, const void *W1,
+               const void *W2, void *Z, void *H, void *Y, void *stream) {
+  Checker c;
+  int64_t nx, nw, nz;
+  c.act(act);
+  c.dtype(dt, true, "tp_mlp_fwd");
+  c.dim(s, "s") && c.dim(h, "h") && c.dim(ft, "ft");
+  c.elems(s, h, nx, "X") && c.elems(h, ft, nw, "W1") && c.elems(s, ft, nz, "Z");
+  c.ptr(X, nx, "X") && c.ptr(W1, nw, "W1") && c.ptr(W2, nw, "W2") && c.ptr(H, nz, "H") && c.ptr(Y, nx, "Y");
+  if (!c.status && act == TP_ACT_GELU) c.ptr(Z, nz, "Z");
+  if (!c.status && Z) c.ptr(Z, nz, "Z");
+  if (c.status) return c.status;
+  hipStream_t st = (hipStream_t)stream;
+  Spec g1 = spec_nn(s, ft, h, EPI_ACT_FWD);
+  Ptrs p1;
+  p1.A[0] = X; p1.lda[0] = h;
+  p1.B[0] = W1; p1.ldb[0] = ft;
+  p1.C[0] = H; p1.ldc[0] = ft;
+  p1.ao0 = Z; p1.ldao = ft;
+  p1.act = act == TP_ACT_GELU ? ACT_GELU : ACT_RELU;
+  if (int e = run(g1, p1, dt, nullptr, st, "tp_mlp_fwd column GEMM")) return e;
+  Spec g2 = spec_nn(s, h, ft, EPI_STORE);
+  Ptrs p2;
+  p2.A[0] = H; p2.lda[0] = ft;
+  p2.B[0] = W2; p2.ldb[0] = h;
+  p2.C[0] = Y; p2.ldc[0] = h;
+  if (int e = run(g2, p2, dt, nullptr, st, "tp_mlp_fwd row GEMM")) return e;
+  return ok();
+}
+
+size_t tp_mlp_bwd_workspace(int dt, int64_t s, int64_t h, int64_t ft) {
+  Checker c;
+  c.dtype(dt, true, "tp_mlp_bwd_workspace");
+  c.dim(s, "s") && c.dim(h, "h") && c.dim(ft, "ft");
+  if (c.status) return 0;
+  return mlp_bwd_layout(dt, s, h, ft).total;
+}
+
+int tp_mlp_bwd(int act, int dt, int64_t s, int64_t h, int64_t ft, const void *X, const void *W1,
+               const void *W2, const void *Z, const void *H, const void *dY, void *dX, void *dW1,
+               void *dW2, void *ws, size_t ws_bytes, void *stream) {
+  Checker c;
+  int64_t nx, nw, nz;
+  c.act(act);
+  c.dtype(dt, true, "tp_mlp_bwd");
+  c.dim(s, "s") && c.dim(h, "h") && c.dim(ft, "ft");
+  c.elems(s, h, nx, "X") && c.elems(h, ft, nw, "W1") && c.elems(s, ft, nz, "Z");
+  c.ptr(X, nx, "X") && c.ptr(W1, nw, "W1") && c.ptr(W2, nw, "W2") && c.ptr(H, nz, "H") &&
+      c.ptr(dY, nx, "dY") && c.ptr(dX, nx, "dX") && c.ptr(dW1, nw, "dW1") && c.ptr(dW2, nw, "dW2");
+  if (!c.status && act == TP_ACT_GELU) c.ptr(Z, nz, "Z");
+  if (!c.status && Z) c.ptr(Z, nz, "Z");
+  if (c.status) return c.status;
+  const MlpBwdLayout L = mlp_bwd_layout(dt, s, h, ft);
+  ws_ok(c, ws, ws_bytes, L.total, "tp_mlp_bwd");
+  if (c.status) return c.status;
+  hipStream_t st = (hipStream_t)stream;
+  char *wsb = (char *)ws;
+  void *dZ = wsb;
+  void *part = wsb + L.dz_bytes;
+  const int a = act == TP_ACT_GELU ? ACT_GELU : ACT_RELU;
+  {  // dZ = (dY . W2^T) * act'(Z)   (ReLU mask from Z, or from H when Z is absent)
+    Ptrs p;
+    p.A[0] = dY; p.lda[0] = h;
+    p.B[0] = W2; p.ldb[0] = h;
+    p.C[0] = dZ; p.ldc[0] = ft;
+    p.ai0 = Z ? Z : H; p.ldai = ft;
+    p.act = a;
+    if (int e = run(L.g_dz, p, dt, part, st, "tp_mlp_bwd dZ GEMM")) return e;
+  }
+  {  // dW2 = H^T . dY
+    Ptrs p;
+    p.A[0] = H; p.lda[0] = ft;
+    p.B[0] = dY; p.ldb[0] = h;
+    p.C[0] = dW2; p.ldc[0] = h;
+    if (int e = run(L.g_dw2, p, dt, part, st, "tp_mlp_bwd dW2 GEMM")) return e;
+  }
+  {  // dX = dZ . W1^T
+    Ptrs p;
+    p.A[0] = dZ; p.lda[0] = ft;
+    p.B[0] = W1; p.ldb[0] = ft;
+    p.C[0] = dX; p.ldc[0] = h;
+    if (int e = run(L.g_dx, p, dt, part, st, "tp_mlp_bwd dX GEMM")) return e;
+  }
+  {  // dW1 = X^T . dZ
+    Ptrs p;
+    p.A[0] = X; p.lda[0] = h;
+    p.B[0] = dZ; p.ldb[0] = ft;
+    p.C[0] = dW1; p.ldc[0] = ft;
+    if (int e = run(L.g_dw1, p, dt, part, st, "tp_mlp_bwd dW1 GEMM")) return e;
+  }
+  return ok();
+}
+
+// ------------------------------------------------------------------ SwiGLU
+int tp_swiglu_fwd(int dt, int64_t s, int64_t h, int64_t ft, const void *X, const void *Wg, const void *Wu,
+                  const void *Wd, void *G, void *U, void *A, void *Y, void *stream) {
+  Checker c;
+  int64_t nx, nw, nz;
+  c.dtype(dt, true, "tp_swiglu_fwd");
+  c.dim(s, "s") && c.dim(h, "h") && c.dim(ft, "ft");
+  c.elems(s, h, nx, "X") && c.elems(h, ft, nw, "Wg") && c.elems(s, ft, nz, "G");
+  c.ptr(X, nx, "X") && c.ptr(Wg, nw, "Wg") && c.ptr(Wu, nw, "Wu") && c.ptr(Wd, nw, "Wd") &&
+      c.ptr(G, nz, "G") && c.ptr(U, nz, "U") && c.ptr(A, nz, "A") && c.ptr(Y, nx, "Y");
+  if (c.status) return c.status;
+  hipStream_t st = (hipStream_t)stream;
+  {  // G = X.Wg, U = X.Wu (one dual-B pass), A = SiLU(G) * U
+    Spec g = spec_nn(s, ft, h, EPI_SWIGLU_FWD);
+    g.dual = true;
+    Ptrs p;
+    p.A[0] = X; p.lda[0] = h;
+    p.B[0] = Wg; p.B[1] = Wu; p.ldb[0] = p.ldb[1] = ft;
+    p.C[0] = A; p.ldc[0] = ft;
+    p.ao0 = G; p.ao1 = U; p.ldao = ft;
+    if (int e = run(g, p, dt, nullptr, st, "tp_swiglu_fwd gate/up GEMM")) return e;
+  }
+  {  // Y = A . Wd
+    Spec g = spec_nn(s, h, ft, EPI_STORE);
+    Ptrs p;
+    p.A[0] = A; p.lda[0] = ft;
+    p.B[0] = Wd; p.ldb[0] = h;
+    p.C[0] = Y; p.ldc[0] = h;
+    if (int e = run(g, p, dt, nullptr, st, "tp_swiglu_fwd down GEMM")) return e;
+  }
+  return ok();
+}
+
+size_t tp_swiglu_bwd_workspace(int dt, int64_t s, int64_t h, int64_t ft) {
+  Checker c;
+  c.dtype(dt, true, "tp_swiglu_bwd_workspace");
+  c.dim(s, "s") && c.dim(h, "h") && c.dim(ft, "ft");
+  if (c.status) return 0;
+  return swiglu_bwd_layout(dt, s, h, ft).total;
+}
+
+int tp_swiglu_bwd(int dt, int64_t s, int64_t h, int64_t ft, const void *X, const void *Wg, const void *Wu,
+                  const void *Wd, const void *G, const void *U, const void *A, const void *dY, void *dX,
+                  void *dWg, void *dWu, void *dWd, void *ws, size_t ws_bytes, void *stream) {
+  Checker c;
+  int64_t nx, nw, nz;
+  c.dtype(dt, true, "tp_swiglu_bwd");
+  c.dim(s, "s") && c.dim(h, "h") && c.dim(ft, "ft");
+  c.elems(s, h, nx, "X") && c.elems(h, ft, nw, "Wg") && c.elems(s, ft, nz, "G");
+  c.ptr(X, nx, "X") && c.ptr(Wg, nw, "Wg") && c.ptr(Wu, nw, "Wu") && c.ptr(Wd, nw, "Wd") &&
+      c.ptr(G, nz, "G") && c.ptr(U, nz, "U") && c.ptr(A, nz, "A") && c.ptr(dY, nx, "dY") &&
+      c.ptr(dX, nx, "dX") && c.ptr(dWg, nw, "dWg") && c.ptr(dWu, nw, "dWu") && c.ptr(dWd, nw, "dWd");
+  if (c.status) return c.status;
+  const SwigluBwdLayout L = swiglu_bwd_layout(dt, s, h, ft);
+  ws_ok(c, ws, ws_bytes, L.total, "tp_swiglu_bwd");
+  if (c.status) return c.status;
+  hipStream_t st = (hipStream_t)stream;
+  char *wsb = (char *)ws;
+  void *dG = wsb, *dU = wsb + L.dg_bytes, *part = wsb + 2 * L.dg_bytes;
+  {  // dA = dY . Wd^T;  dG = dA * U * SiLU'(G);  dU = dA * SiLU(G)
+    Ptrs p;
+    p.A[0] = dY; p.lda[0] = h;
+    p.B[0] = Wd; p.ldb[0] = h;
+    p.C[0] = dG; p.ldc[0] = ft;
+    p.ai0 = G; p.ai1 = U; p.ldai = ft;
+    p.ao0 = dU; p.ldao = ft;
+    if (int e = run(L.g_da, p, dt, part, st, "tp_swiglu_bwd dA GEMM")) return e;
+  }
+  {  // dWd = A^T . dY
+    Ptrs p;
+    p.A[0] = A; p.lda[0] = ft;
+    p.B[0] = dY; p.ldb[0] = h;
+    p.C[0] = dWd; p.ldc[0] = h;
+    if (int e = run(L.g_dwd, p, dt, part, st, "tp_swiglu_bwd dWd GEMM")) return e;
+  }
+  {  // dX = dG . Wg^T + dU . Wu^T
+    Ptrs p;
+    p.A[0] = dG; p.A[1] = dU; p.lda[0] = p.lda[1] = ft;
+    p.B[0] = Wg; p.B[1] = Wu; p.ldb[0] = p.ldb[1] = ft;
+    p.C[0] = dX; p.ldc[0] = h;
+    if (int e = run(L.g_dx, p, dt, part, st, "tp_swiglu_bwd dX GEMM")) return e;
+  }
+  {  // [dWg | dWu] = X^T . [dG | dU]
+    Ptrs p;
+    p.A[0] = X; p.lda[0] = h;
+    p.B[0] = dG; p.B[1] = dU; p.ldb[0] = p.ldb[1] = ft;
+    p.C[0] = dWg; p.C[1] = dWu; p.ldc[0] = p.ldc[1] = ft;
+    if (int e = run(L.g_dwgu, p, dt, part, st, "tp_swiglu_bwd dWg/dWu GEMM")) return e;
+  }
+  return ok();
+}
+
+// ------------------------------------------------------------------ attention projections
+int tp_attn_proj_fwd(int dt, int64_t s, int64_t h, int64_t dq, int64_t dkv, const void *X, const void *Wq,
+                     const void *Wk, const void *Wv, const void *O, const void *Wo, void *Q, void *K, void *V,
+                     void *Y, void *stream) {
+  Checker c;
+  int64_t nx, nwq, nwk, nq, nk;
+  c.dtype(dt, true, "tp_attn_proj_fwd");
+  c.dim(s, "s") && c.dim(h, "h") && c.dim(dq, "dq") && c.dim(dkv, "dkv");
+  c.elems(s, h, nx, "X") && c.elems(h, dq, nwq, "Wq") && c.elems(h, dkv, nwk, "Wk") &&
+      c.elems(s, dq, nq, "Q") && c.elems(s, dkv, nk, "K");
+  c.ptr(X, nx, "X") && c.ptr(Wq, nwq, "Wq") && c.ptr(Wk, nwk, "Wk") && c.ptr(Wv, nwk, "Wv") &&
+      c.ptr(O, nq, "O") && c.ptr(Wo, nwq, "Wo") && c.ptr(Q, nq, "Q") && c.ptr(K, nk, "K") &&
+      c.ptr(V, nk, "V") && c.ptr(Y, nx, "Y");
+  if (c.status) return c.status;
+  hipStream_t st = (hipStream_t)stream;
+  {  // [Q | K | V] = X . [Wq | Wk | Wv]: one launch, three N-segments
+    Spec g;
+    g.layout = GEMM_NN;
+    g.epi = EPI_STORE;
+    g.M = s;
+    g.K = h;
+    g.nseg = 3;
+    g.seg[0] = dq;
+    g.seg[1] = g.seg[2] = dkv;
+    g.N = dq + 2 * dkv;
+    g.ld(h);
+    g.ld(dq);
+    g.ld(dkv);
+    Ptrs p;
+    p.A[0] = X; p.lda[0] = h;
+    p.B[0] = Wq; p.B[1] = Wk; p.B[2] = Wv;
+    p.ldb[0] = dq; p.ldb[1] = p.ldb[2] = dkv;
+    p.C[0] = Q; p.C[1] = K; p.C[2] = V;
+    p.ldc[0] = dq; p.ldc[1] = p.ldc[2] = dkv;
+    if (int e = run(g, p, dt, nullptr, st, "tp_attn_proj_fwd QKV GEMM")) return e;
+  }
+  {  // Y = O . Wo
+    Spec g = spec_nn(s, h, dq, EPI_STORE);
+    Ptrs p;
+    p.A[0] = O; p.lda[0] = dq;
+    p.B[0] = Wo; p.ldb[0] = h;
+    p.C[0] = Y; p.ldc[0] = h;
+    if (int e = run(g, p, dt, nullptr, st, "tp_attn_proj_fwd output GEMM")) return e;
+  }
+  return ok();
+}
+
+size_t tp_attn_proj_bwd_workspace(int dt, int64_t s, int64_t h, int64_t dq, int64_t dkv) {
+  Checker c;
+  c.dtype(dt, true, "tp_attn_proj_bwd_workspace");
+  c.dim(s, "s") && c.dim(h, "h") && c.dim(dq, "dq") && c.dim(dkv, "dkv");
+  if (c.status) return 0;
+  return attn_bwd_layout(dt, s, h, dq, dkv).total;
+}
+
+int tp_attn_proj_bwd(int dt, int64_t s, int64_t h, int64_t dq, int64_t dkv, const void *X, const void *Wq,
+                     const void *Wk, const void *Wv, const void *O, const void *Wo, const void *dQ,
+                     const void *dK, const void *dV, const void *dY, void *dX, void *dWq, void *dWk,
+                     void *dWv, void *dO, void *dWo, void *ws, size_t ws_bytes, void *stream) {
+  Checker c;
+  int64_t nx, nwq, nwk, nq, nk;
+  c.dtype(dt, true, "tp_attn_proj_bwd");
+  c.dim(s, "s") && c.dim(h, "h") && c.dim(dq, "dq") && c.dim(dkv, "dkv");
+  c.elems(s, h, nx, "X") && c.elems(h, dq, nwq, "Wq") && c.elems(h, dkv, nwk, "Wk") &&
+      c.elems(s, dq, nq, "Q") && c.elems(s, dkv, nk, "K");
+  c.ptr(X, nx, "X") && c.ptr(Wq, nwq, "Wq") && c.ptr(Wk, nwk, "Wk") && c.ptr(Wv, nwk, "Wv") &&
+      c.ptr(O, nq, "O") && c.ptr(Wo, nwq, "Wo") && c.ptr(dQ, nq, "dQ") && c.ptr(dK, nk, "dK") &&
+      c.ptr(dV, nk, "dV") && c.ptr(dY, nx, "dY") && c.ptr(dX, nx, "dX") && c.ptr(dWq, nwq, "dWq") &&
+      c.ptr(dWk, nwk, "dWk") && c.ptr(dWv, nwk, "dWv") && c.ptr(dO, nq, "dO") && c.ptr(dWo, nwq, "dWo");
+  if (c.status) return c.status;
+  const AttnBwdLayout L = attn_bwd_layout(dt, s, h, dq, dkv);
+  ws_ok(c, ws, ws_bytes, L.total, "tp_attn_proj_bwd");
+  if (c.status) return c.status;
+  hipStream_t st = (hipStream_t)stream;
+  {  // dX = dQ.Wq^T + dK.Wk^T + dV.Wv^T: one launch, three K-segments
+    Ptrs p;
+    p.A[0] = dQ; p.A[1] = dK; p.A[2] = dV;
+    p.lda[0] = dq; p.lda[1] = p.lda[2] = dkv;
+    p.B[0] = Wq; p.B[1] = Wk; p.B[2] = Wv;
+    p.ldb[0] = dq; p.ldb[1] = p.ldb[2] = dkv;
+    p.C[0] = dX; p.ldc[0] = h;
+    if (int e = run(L.g_dx, p, dt, ws, st, "tp_attn_proj_bwd dX GEMM")) return e;
+  }
+  {  // [dWq | dWk | dWv] = X^T . [dQ | dK | dV]
+    Ptrs p;
+    p.A[0] = X; p.lda[0] = h;
+    p.B[0] = dQ; p.B[1] = dK; p.B[2] = dV;
+    p.ldb[0] = dq; p.ldb[1] = p.ldb[2] = dkv;
+    p.C[0] = dWq; p.C[1] = dWk; p.C[2] = dWv;
+    p.ldc[0] = dq; p.ldc[1] = p.ldc[2] = dkv;
+    if (int e = run(L.g_dwqkv, p, dt, ws, st, "tp_attn_proj_bwd dWqkv GEMM")) return e;
+  }
+  {  // dO = dY . Wo^T
+    Ptrs p;
+    p.A[0] = dY; p.lda[0] = h;
+    p.B[0] = Wo; p.ldb[0] = h;
+    p.C[0] = dO; p.ldc[0] = dq;
+    if (int e = run(L.g_do, p, dt, ws, st, "tp_attn_proj_bwd dO GEMM")) return e;
+  }
+  {  // dWo = O^T . dY
+    Ptrs p;
+    p.A[0] = O; p.lda[0] = dq;
+    p.B[0] = dY; p.ldb[0] = h;
+    p.C[0] = dWo; p.ldc[0] = h;
+    if (int e = run(L.g_dwo, p, dt, ws, st, "tp_attn_proj_bwd dWo GEMM")) return e;
+  }
+  return ok();
+}
+
+// ------------------------------------------------------------------ vocab
+int tp_lm_head_fwd(int dt, int64_t s, int64_t h, int64_t Vs, const void *Hf, const void *Wlm, float *logits,
+                   void *stream) {
+  Checker c;
+  int64_t nh, nw, nl;
+  c.dtype(dt, true, "tp_lm_head_fwd");
+  c.dim(s, "s") && c.dim(h, "h") && c.dim(Vs, "Vs");
+  c.elems(s, h, nh, "Hf") && c.elems(h, Vs, nw, "Wlm") && c.elems(s, Vs, nl, "logits");
+  c.ptr(Hf, nh, "Hf") && c.ptr(Wlm, nw, "Wlm") && c.ptr(logits, nl, "logits");
+  if (c.status) return c.status;
+  Spec g = spec_nn(s, Vs, h, EPI_STORE);
+  g.out_f32 = true;
+  Ptrs p;
+  p.A[0] = Hf; p.lda[0] = h;
+  p.B[0] = Wlm; p.ldb[0] = Vs;
+  p.C[0] = logits; p.ldc[0] = Vs;
+  if (int e = run(g, p, dt, nullptr, (hipStream_t)stream, "tp_lm_head_fwd GEMM")) return e;
+  return ok();
+}
+
+int tp_vocab_ce(int64_t s, int64_t Vs, int64_t vocab_start, const float *logits, const int64_t *target,
+                float *lmax, float *lsumexp, float *tlogit, void *stream) {
+  Checker c;
+  int64_t nl;
+  c.dim(s, "s") && c.dim(Vs, "Vs");
+  if (!c.status && vocab_start < 0) c.status = fail(TP_ESHAPE, "vocab_start = %lld < 0", (long long)vocab_start);
+  c.elems(s, Vs, nl, "logits");
+  c.ptr(logits, nl, "logits") && c.ptr(target, s, "target") && c.ptr(lmax, s, "lmax") &&
+      c.ptr(lsumexp, s, "lsumexp") && c.ptr(tlogit, s, "tlogit");
+  if (c.status) return c.status;
+  hipError_t e = tp_launch_vocab_ce(s, Vs, vocab_start, logits, target, lmax, lsumexp, tlogit,
+                                    (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TP_EHIP, "tp_vocab_ce: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int tp_vocab_embed(int dt, int64_t n, int64_t Vs, int64_t h, int64_t vocab_start, const int64_t *ids,
+                   const void *table, void *out, void *stream) {
+  Checker c;
+  int64_t nt, no;
+  c.dtype(dt, true, "tp_vocab_embed");
+  c.dim(n, "n") && c.dim(Vs, "Vs") && c.dim(h, "h");
+  if (!c.status && vocab_start < 0) c.status = fail(TP_ESHAPE, "vocab_start = %lld < 0", (long long)vocab_start);
+  c.elems(Vs, h, nt, "table") && c.elems(n, h, no, "out");
+  c.ptr(ids, n, "ids") && c.ptr(table, nt, "table") && c.ptr(out, no, "out");
+  if (c.status) return c.status;
+  hipError_t e = tp_launch_vocab_embed((int)esize(dt), n, Vs, h, vocab_start, ids, table, out,
+                                       (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TP_EHIP, "tp_vocab_embed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,150 @@
+// vocab.hip -- vocab-parallel cross-entropy statistics and embedding gather.
+//
+// Cross entropy split by vocab (lecture 16 notes §5.5; book "7.3 模型并行与张
+// 量并行" §7.3.4): each shard reduces its own [s, V/t] logit slice to three
+// numbers per position -- the row max, the sum of exp(z - max) and the target's
+// logit when the target id falls in the shard -- so only 3 scalars per token
+// ever leave the device instead of the logits.
+//
+// The embedding split by vocab returns the table row for ids inside the
+// shard and a zero vector otherwise; summing over shards restores the lookup.
+//
+// Both are HBM-streaming kernels.  The CE kernel gives each row to one
+// 256-thread workgroup which issues all of its 16-byte loads for the row up
+// front (16 per thread covers a 16384-float row), takes the exact row max,
+// then sums exp(z - max) from registers: the logits are read from HBM once.
+#include "launch.h"
+
+namespace {
+
+constexpr int CE_THREADS = 256;
+constexpr int CE_PER = 16;  // 16-byte vectors held per thread per pass
+constexpr float LOG2E = 1.4426950408889634f;
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// VW = 4: rows are 16-byte aligned (Vs % 4 == 0); VW = 1: any Vs.
+template <int VW>
+__global__ void __launch_bounds__(CE_THREADS) vocab_ce_kernel(const float *__restrict__ z,
+                                                              const int64_t *__restrict__ tgt,
+                                                              int64_t s, int64_t Vs, int64_t start,
+                                                              float *__restrict__ m_out,
+                                                              float *__restrict__ se_out,
+                                                              float *__restrict__ tl_out) {
+  typedef float vec_t __attribute__((ext_vector_type(VW)));
+  __shared__ float red[CE_THREADS / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int64_t nvec = Vs / VW;
+  for (int64_t row = blockIdx.x; row < s; row += gridDim.x) {
+    const vec_t *p = (const vec_t *)(z + row * Vs);
+    float run_m = -INFINITY, run_s = 0.f;
+    for (int64_t base = 0; base < nvec; base += (int64_t)CE_THREADS * CE_PER) {
+      vec_t v[CE_PER];
+#pragma unroll
+      for (int i = 0; i < CE_PER; ++i) {
+        const int64_t idx = base + tid + (int64_t)CE_THREADS * i;
+        if (idx < nvec) v[i] = p[idx];
+        else
+#pragma unroll
+          for (int e = 0; e < VW; ++e) v[i][e] = -INFINITY;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < CE_PER; ++i)
+#pragma unroll
+        for (int e = 0; e < VW; ++e) mx = fmaxf(mx, v[i][e]);
+      mx = wave_max(mx);
+      if (lane == 0) red[wid] = mx;
+      __syncthreads();
+      mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+      __syncthreads();
+      const float new_m = fmaxf(run_m, mx);
+      float sum = 0.f;
+      if (new_m != -INFINITY) {
+        const float mb = new_m * LOG2E;
+#pragma unroll
+        for (int i = 0; i < CE_PER; ++i)
+#pragma unroll
+          for (int e = 0; e < VW; ++e) sum += exp2f(fmaf(v[i][e], LOG2E, -mb));
+      }
+      sum = wave_sum(sum);
+      if (lane == 0) red[wid] = sum;
+      __syncthreads();
+      sum = (red[0] + red[1]) + (red[2] + red[3]);
+      __syncthreads();
+      // rescale the running sum when a later pass raises the max (rows > 16384 floats)
+      run_s = (run_s == 0.f ? 0.f : run_s * exp2f((run_m - new_m) * LOG2E)) + sum;
+      run_m = new_m;
+    }
+    if (tid == 0) {
+      const int64_t y = tgt[row];
+      m_out[row] = run_m;
+      se_out[row] = run_s;
+      tl_out[row] = (y >= start && y - start < Vs) ? z[row * Vs + (y - start)] : 0.f;
+    }
+  }
+}
+
+// One workgroup per output row: copy the owned table row, or write zeros.
+template <typename T>
+__global__ void __launch_bounds__(256) vocab_embed_kernel(int64_t n, int64_t Vs, int64_t nelem,
+                                                          int64_t start,
+                                                          const int64_t *__restrict__ ids,
+                                                          const T *__restrict__ table,
+                                                          T *__restrict__ out) {
+  for (int64_t r = blockIdx.x; r < n; r += gridDim.x) {
+    const int64_t id = ids[r];
+    const bool in = id >= start && id - start < Vs;
+    T *dst = out + r * nelem;
+    if (in) {
+      const T *src = table + (id - start) * nelem;
+      for (int64_t i = threadIdx.x; i < nelem; i += blockDim.x) dst[i] = src[i];
+    } else {
+      T zero;
+      __builtin_memset(&zero, 0, sizeof(T));
+      for (int64_t i = threadIdx.x; i < nelem; i += blockDim.x) dst[i] = zero;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t tp_launch_vocab_ce(int64_t s, int64_t Vs, int64_t start, const float *z, const int64_t *tgt,
+                              float *m, float *se, float *tl, hipStream_t st) {
+  if (s == 0) return hipSuccess;
+  const unsigned grid = (unsigned)(s < 1048576 ? s : 1048576);
+  const bool v4 = (Vs % 4 == 0) && (((uintptr_t)z & 15) == 0);
+  if (v4)
+    hipLaunchKernelGGL(vocab_ce_kernel<4>, dim3(grid), dim3(CE_THREADS), 0, st, z, tgt, s, Vs, start, m, se, tl);
+  else
+    hipLaunchKernelGGL(vocab_ce_kernel<1>, dim3(grid), dim3(CE_THREADS), 0, st, z, tgt, s, Vs, start, m, se, tl);
+  return hipGetLastError();
+}
+
+hipError_t tp_launch_vocab_embed(int elem_bytes, int64_t n, int64_t Vs, int64_t h, int64_t start,
+                                 const int64_t *ids, const void *table, void *out, hipStream_t st) {
+  if (n == 0 || h == 0) return hipSuccess;
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const int64_t bytes = h * elem_bytes;
+  const unsigned grid = (unsigned)(n < 1048576 ? n : 1048576);
+  const bool aligned = (((uintptr_t)table | (uintptr_t)out) & 15) == 0;
+  if (aligned && bytes % 16 == 0)
+    hipLaunchKernelGGL(vocab_embed_kernel<u32x4>, dim3(grid), dim3(256), 0, st, n, Vs, bytes / 16, start, ids,
+                       (const u32x4 *)table, (u32x4 *)out);
+  else if (elem_bytes == 4)
+    hipLaunchKernelGGL(vocab_embed_kernel<uint32_t>, dim3(grid), dim3(256), 0, st, n, Vs, h, start, ids,
+                       (const uint32_t *)table, (uint32_t *)out);
+  else
+    hipLaunchKernelGGL(vocab_embed_kernel<uint16_t>, dim3(grid), dim3(256), 0, st, n, Vs, h, start, ids,
+                       (const uint16_t *)table, (uint16_t *)out);
+  return hipGetLastError();
+}

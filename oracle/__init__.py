@@ -52,7 +52,7 @@ def _L():
     global _lib
     if _lib is None:
         lib = ctypes.CDLL(build())
-        lib.or_gemm.argtypes = [_i64, _i64, _i64, _d, _i64, _i64, _d, _i64, _i64, _d]
+        lib.or_gemm.argtypes = [_i64, _i64, _i64, _d, _d, _d]
         lib.or_act.argtypes = [ctypes.c_int, _i64, _d, _d]
         lib.or_act_grad.argtypes = [ctypes.c_int, _i64, _d, _d]
         lib.or_ce_stats.argtypes = [_i64, _i64, _i64, _d, ctypes.c_void_p, _d, _d, _d]
@@ -84,22 +84,14 @@ def _p(a: np.ndarray):
 # primitives
 # ---------------------------------------------------------------------------
 def matmul(A, B, ta: bool = False, tb: bool = False) -> np.ndarray:
-    """op(A) . op(B) in fp64, op = transpose when asked.  A, B are 2-D arrays
-    stored row-major as given; a transposed operand is read through strides."""
-    A = _f64(A)
-    B = _f64(B)
-    if ta:
-        K, M = A.shape
-        a_rs, a_cs = 1, M
-    else:
-        M, K = A.shape
-        a_rs, a_cs = K, 1
-    if tb:
-        N, K2 = B.shape
-        b_rs, b_cs = 1, K2
-    else:
-        K2, N = B.shape
-        b_rs, b_cs = N, 1
+    """op(A) . op(B) in fp64, op = transpose when asked; every entry is one dot
+    product summed over k in increasing order (oracle.c or_gemm)."""
+    A = np.asarray(A, dtype=np.float64)
+    B = np.asarray(B, dtype=np.float64)
+    Am = np.ascontiguousarray(A.T if ta else A)          # [M, K]
+    Bt = np.ascontiguousarray(B if tb else B.T)          # [N, K]
+    M, K = Am.shape
+    N, K2 = Bt.shape
     if K != K2:
         raise ValueError(f"inner sizes differ: {K} vs {K2}")
     C = np.empty((M, N), dtype=np.float64)
@@ -107,7 +99,7 @@ def matmul(A, B, ta: bool = False, tb: bool = False) -> np.ndarray:
         if K == 0:
             C[...] = 0.0
         else:
-            _L().or_gemm(M, N, K, _p(A), a_rs, a_cs, _p(B), b_rs, b_cs, _p(C))
+            _L().or_gemm(M, N, K, _p(Am), _p(Bt), _p(C))
     return C
 
 

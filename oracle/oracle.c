@@ -31,20 +31,21 @@
 /* dense product                                                           */
 /* ---------------------------------------------------------------------- */
 
-/* C[i,j] = sum_{k=0}^{K-1} A(i,k) * B(k,j), with A(i,k) = A[i*a_rs + k*a_cs]
- * and B(k,j) = B[k*b_rs + j*b_cs]; C is row-major [M,N].  The strides let
- * the same definition express X.W, dY.W^T and X^T.dZ without copying. */
+/* C[i,j] = sum_{k=0}^{K-1} A[i,k] * B[k,j], summed over k in increasing
+ * order.  A is row-major [M,K]; the right operand is passed transposed, Bt =
+ * B^T row-major [N,K], so every dot product reads two contiguous rows.  The
+ * caller makes transposed views contiguous first: a copy, no arithmetic. */
 void or_gemm(int64_t M, int64_t N, int64_t K,
-             const double *A, int64_t a_rs, int64_t a_cs,
-             const double *B, int64_t b_rs, int64_t b_cs,
-             double *C)
+             const double *A, const double *Bt, double *C)
 {
     #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < M; ++i) {
+        const double *a = A + i * K;
         for (int64_t j = 0; j < N; ++j) {
+            const double *b = Bt + j * K;
             double acc = 0.0;
             for (int64_t k = 0; k < K; ++k)
-                acc += A[i * a_rs + k * a_cs] * B[k * b_rs + j * b_cs];
+                acc += a[k] * b[k];
             C[i * N + j] = acc;
         }
     }

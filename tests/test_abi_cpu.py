@@ -1,0 +1,121 @@
+"""CPU checks of the C ABI: the library loads, exports every entry point the
+header declares, and rejects bad arguments before anything reaches the GPU.
+
+No call here launches a kernel: every call either fails validation or has
+nothing to compute (an empty batch), so these run without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from megatron_tensor_layer_tp_amd import tpshard as T
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tpshard.h")
+
+A16 = 1 << 20  # a fake, 16-byte aligned "device address" that validation never dereferences
+
+
+def header_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(tp_\w+)\s*\(", txt, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(T.LIB_PATH):
+        from megatron_tensor_layer_tp_amd import build
+        build.build(verbose=False)
+    return T.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = header_functions()
+    assert len(names) == 15, names
+    raw = ctypes.CDLL(T.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+    assert set(names) == set(T.EXPORTS)
+    assert T.tp_abi_version() == 1
+    assert T.tp_status_string(T.TP_ESHAPE) == "TP_ESHAPE"
+    assert T.tp_status_string(99) == "TP_UNKNOWN_STATUS"
+
+
+def _st(L, name, *args):
+    return getattr(L, name)(*args)
+
+
+def mlp_args(**kw):
+    a = dict(act=T.TP_ACT_GELU, dt=T.TP_DT_BF16, s=8, h=16, ft=32, X=A16, W1=A16, W2=A16, Z=A16,
+             H=A16, Y=A16, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+def test_mlp_fwd_validation(L):
+    assert _st(L, "tp_mlp_fwd", *mlp_args(act=7)) == T.TP_EINVAL
+    assert "act 7" in T.tp_last_error()
+    assert _st(L, "tp_mlp_fwd", *mlp_args(dt=5)) == T.TP_EINVAL
+    assert _st(L, "tp_mlp_fwd", *mlp_args(s=-1)) == T.TP_ESHAPE
+    assert "s = -1" in T.tp_last_error()
+    assert _st(L, "tp_mlp_fwd", *mlp_args(h=1 << 31)) == T.TP_ESHAPE
+    assert _st(L, "tp_mlp_fwd", *mlp_args(X=None)) == T.TP_EINVAL
+    assert "X is NULL" in T.tp_last_error()
+    assert _st(L, "tp_mlp_fwd", *mlp_args(W2=A16 + 2)) == T.TP_EALIGN
+    # GeLU needs the pre-activation Z; ReLU may drop it
+    assert _st(L, "tp_mlp_fwd", *mlp_args(Z=None)) == T.TP_EINVAL
+    # an empty batch is legal and has nothing to do (no launch, no GPU needed)
+    assert _st(L, "tp_mlp_fwd", *mlp_args(s=0, X=None, Z=None, H=None, Y=None, act=T.TP_ACT_RELU)) == T.TP_OK
+    assert T.tp_last_error() == ""
+
+
+def test_bwd_workspace_rules(L):
+    need = T.tp_mlp_bwd_workspace(T.TP_DT_BF16, 8192, 768, 1536)
+    assert need >= 8192 * 1536 * 2          # dZ is staged in the workspace
+    assert T.tp_mlp_bwd_workspace(T.TP_DT_F32, 8, 16, 32) >= 8 * 32 * 4
+    assert T.tp_mlp_bwd_workspace(T.TP_DT_BF16, -1, 16, 32) == 0
+    args = [T.TP_ACT_RELU, T.TP_DT_BF16, 8192, 768, 1536] + [A16] * 9
+    assert _st(L, "tp_mlp_bwd", *args, None, 0, None) == T.TP_EWORKSPACE
+    assert _st(L, "tp_mlp_bwd", *args, A16, need - 1, None) == T.TP_EWORKSPACE
+    assert _st(L, "tp_mlp_bwd", *args, A16 + 16, need, None) == T.TP_EALIGN
+    assert T.tp_swiglu_bwd_workspace(T.TP_DT_BF16, 8192, 8192, 3584) >= 2 * 8192 * 3584 * 2
+    assert T.tp_attn_proj_bwd_workspace(T.TP_DT_BF16, 8192, 8192, 1024, 128) >= 0
+    # the query is a pure function of the sizes
+    assert need == T.tp_mlp_bwd_workspace(T.TP_DT_BF16, 8192, 768, 1536)
+
+
+def test_vocab_validation(L):
+    ce = [16, 32, 0, A16, A16, A16, A16, A16, None]
+    bad = list(ce)
+    bad[2] = -5
+    assert _st(L, "tp_vocab_ce", *bad) == T.TP_ESHAPE
+    bad = list(ce)
+    bad[4] = None
+    assert _st(L, "tp_vocab_ce", *bad) == T.TP_EINVAL
+    assert _st(L, "tp_vocab_ce", 0, 32, 0, None, None, None, None, None, None) == T.TP_OK
+    em = [T.TP_DT_BF16, 16, 32, 64, 0, A16, A16, A16, None]
+    bad = list(em)
+    bad[0] = 9
+    assert _st(L, "tp_vocab_embed", *bad) == T.TP_EINVAL
+    bad = list(em)
+    bad[7] = A16 + 8
+    assert _st(L, "tp_vocab_embed", *bad) == T.TP_EALIGN
+    assert _st(L, "tp_lm_head_fwd", T.TP_DT_BF16, 8, -2, 16, A16, A16, A16, None) == T.TP_ESHAPE
+
+
+def test_layer_calls_validation(L):
+    sw = [T.TP_DT_BF16, 8, 16, 32] + [A16] * 8 + [None]
+    bad = list(sw)
+    bad[6] = None  # Wu
+    assert _st(L, "tp_swiglu_fwd", *bad) == T.TP_EINVAL
+    assert "Wu" in T.tp_last_error()
+    at = [T.TP_DT_BF16, 8, 16, 16, 8] + [A16] * 10 + [None]
+    bad = list(at)
+    bad[4] = -8
+    assert _st(L, "tp_attn_proj_fwd", *bad) == T.TP_ESHAPE
+    # zero-width K/V heads are legal sizes (nothing to write for them)
+    ok = [T.TP_DT_BF16, 0, 16, 16, 0] + [A16, A16, None, None, None, A16, A16, None, None, None] + [None]
+    assert _st(L, "tp_attn_proj_fwd", *ok) == T.TP_OK

@@ -1,0 +1,154 @@
+"""GPU parity of the vocab-parallel calls ("7.3 模型并行与张量并行" §7.3.4;
+lecture 16 notes §5.5) against the fp64 oracle.
+
+  * LM head: fp32 logits, relative Frobenius error <= 5e-3 (full at small
+    sizes, sampled rows at the [8192,8192] x [8192,16032] shard).
+  * CE statistics on seeded fp32 logit slices: max and target logit bit-exact,
+    sum of exponentials <= 1e-5 relative, and the loss combined over all 8
+    shards within 1e-4 absolute of the direct logsumexp - z[target].
+  * Embedding: bit-exact rows, zero rows for ids outside the shard.
+"""
+import numpy as np
+import pytest
+
+from gpu_util import dev, fill_garbage, host, host_f64, need_gpu, rel_fro, torch
+from megatron_tensor_layer_tp_amd import inputs as I
+from megatron_tensor_layer_tp_amd import tpshard as T
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+    T.lib()
+
+
+def bf(a):
+    return I.f32_to_bf16_bits(np.asarray(a, np.float32))
+
+
+# ---------------------------------------------------------------- LM head
+def run_lm(Hf, W):
+    s, h = Hf.shape
+    Vs = W.shape[1]
+    out = fill_garbage(torch.empty((s, Vs), dtype=torch.float32, device="cuda:0"))
+    T.tp_lm_head_fwd(T.TP_DT_BF16, s, h, Vs, dev(Hf), dev(W), out)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("s,h,Vs", [(136, 128, 200), (64, 256, 16032 // 16), (300, 72, 1001)])
+def test_lm_head_small(oracle_mod, s, h, Vs):
+    g = np.random.default_rng(s)
+    Hf, W = bf(g.standard_normal((s, h))), bf(g.standard_normal((h, Vs)) * 0.05)
+    got = host_f64(run_lm(Hf, W))
+    want = oracle_mod.lm_head(I.bf16_bits_to_f64(Hf), I.bf16_bits_to_f64(W))
+    assert rel_fro(got, want) <= 5e-3
+    # fp32 logits out of an fp32 accumulation are far better than the bar
+    assert rel_fro(got, want) <= 1e-5
+
+
+def test_lm_head_vocab_shard_sampled(oracle_mod):
+    d = I.vocab_inputs(5, with_table=False, with_logits=False)
+    got = run_lm(d["Hf"], d["Wlm"][0])
+    rows = I.sample_rows(d["s"], 32, 5, 21)
+    want = oracle_mod.lm_head_rows(I.bf16_bits_to_f64(d["Hf"]), I.bf16_bits_to_f64(d["Wlm"][0]), rows)
+    err = rel_fro(host_f64(got)[rows], want)
+    assert err <= 1e-5, err
+
+
+# ---------------------------------------------------------------- CE statistics
+def run_ce(z, tgt, start):
+    s, Vs = z.shape
+    zd = dev(np.ascontiguousarray(z, np.float32))
+    td = dev(np.ascontiguousarray(tgt, np.int64))
+    m, se, tl = (fill_garbage(torch.empty(s, dtype=torch.float32, device="cuda:0")) for _ in range(3))
+    T.tp_vocab_ce(s, Vs, start, zd, td, m, se, tl)
+    torch.cuda.synchronize()
+    return host(m), host(se), host(tl)
+
+
+def check_ce(oracle_mod, z, tgt, start):
+    m, se, tl = run_ce(z, tgt, start)
+    om, ose, otl = oracle_mod.ce_stats(z.astype(np.float64), tgt, start)
+    assert np.array_equal(m.astype(np.float64), om)
+    assert np.array_equal(tl.astype(np.float64), otl)
+    ok = ose > 0
+    assert np.all(se[~ok] == 0)
+    rel = np.abs(se[ok] - ose[ok]) / ose[ok]
+    assert rel.max(initial=0) <= 1e-5, rel.max()
+    return m, se, tl
+
+
+@pytest.mark.parametrize("s,Vs,start", [(7, 1, 0), (33, 1001, 5), (64, 16032, 16032 * 3),
+                                        (16, 40000, 0), (5, 3, 2), (9, 0, 4)])
+def test_ce_edge_shapes(oracle_mod, s, Vs, start):
+    g = np.random.default_rng(Vs + s)
+    z = (g.standard_normal((s, Vs)) * 3).astype(np.float32)
+    tgt = g.integers(-3, start + Vs + 4, s).astype(np.int64)
+    if s > 2:
+        tgt[0] = start                # first in-shard id
+        tgt[1] = start + Vs - 1       # last in-shard id
+    check_ce(oracle_mod, z, tgt, start)
+
+
+def test_ce_vocab_shard_full(oracle_mod):
+    d = I.vocab_inputs(5, shards=[0, 7], with_lm=False, with_table=False)
+    for i in (0, 7):
+        check_ce(oracle_mod, d["logits"][i], d["targets"], i * d["Vs"])
+
+
+def test_ce_loss_combined_over_shards(oracle_mod):
+    """All 8 vocab shards of V=128256 for 256 positions: the per-shard GPU
+    statistics, combined, give the direct loss within 1e-4 absolute."""
+    s, V, t = 256, 128256, 8
+    Vs = V // t
+    g = np.random.default_rng(42)
+    z = (g.standard_normal((s, V)) * 0.905).astype(np.float32)
+    tgt = I.ids_uniform(s, V, 5, I.T_TGT)
+    ms, ses, tls = [], [], []
+    for i in range(t):
+        m, se, tl = run_ce(np.ascontiguousarray(z[:, i * Vs:(i + 1) * Vs]), tgt, i * Vs)
+        ms.append(m)
+        ses.append(se)
+        tls.append(tl)
+    loss = oracle_mod.ce_combine(ms, ses, tls)
+    direct = oracle_mod.ce_direct(z.astype(np.float64), tgt)
+    assert np.abs(loss - direct).max() <= 1e-4
+    assert abs(loss.mean() - direct.mean()) <= 1e-4
+
+
+# ---------------------------------------------------------------- embedding
+def run_embed(ids, table, start, bf16=True):
+    n = ids.shape[0]
+    Vs, h = table.shape
+    out = torch.empty((n, h), dtype=torch.int16 if bf16 else torch.float32, device="cuda:0")
+    out.fill_(0x7fc1 if bf16 else float("nan"))
+    T.tp_vocab_embed(T.TP_DT_BF16 if bf16 else T.TP_DT_F32, n, Vs, h, start, dev(ids), dev(table), out)
+    torch.cuda.synchronize()
+    return host(out)
+
+
+def test_embed_vocab_shard_bit_exact(oracle_mod):
+    d = I.vocab_inputs(5, shards=[0, 3], with_lm=False, with_logits=False)
+    for i in (0, 3):
+        got = run_embed(d["ids"], d["table"][i], i * d["Vs"])
+        want = oracle_mod.embed(d["ids"], d["table"][i], i * d["Vs"])
+        assert np.array_equal(got, want)
+        inside = (d["ids"] >= i * d["Vs"]) & (d["ids"] < (i + 1) * d["Vs"])
+        assert inside.sum() > 0 and np.all(got[~inside] == 0)
+
+
+@pytest.mark.parametrize("h,bf16", [(7, True), (12, True), (5, False), (64, False), (1, True)])
+def test_embed_odd_rows(oracle_mod, h, bf16):
+    g = np.random.default_rng(h)
+    Vs, n, start = 37, 200, 100
+    if bf16:
+        table = bf(g.standard_normal((Vs, h)) + 3)
+    else:
+        table = (g.standard_normal((Vs, h)) + 3).astype(np.float32)
+    ids = g.integers(-5, 200, n).astype(np.int64)
+    ids[:3] = [start, start + Vs - 1, start + Vs]
+    got = run_embed(ids, table, start, bf16)
+    assert np.array_equal(got.view(np.uint8), oracle_mod.embed(ids, table, start).view(np.uint8))
