@@ -1,0 +1,313 @@
+#!/usr/bin/env python3
+"""Benchmark of the tensor-parallel shard path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--rows all|mlp] [--no-cpu-baseline]
+
+A step is one pass over every step of the shard path on seeded synthetic
+inputs already resident in HBM:
+  * MLP shard forward + backward (column GEMM + GeLU, row GEMM, and the dZ /
+    dW2 / dX / dW1 GEMMs) at the GPT-2-small t=2 shard: s=8*1024, h=768,
+    f/t=1536 -- the workload the headline metric is quoted on;
+  * SwiGLU shard and attention projections, forward + backward, at the
+    Llama-3-70B t=8 shard (s=8192, h=8192, f/t=3584, dq=1024, dkv=128);
+  * vocab shard at V=128256, t=8: LM-head GEMM (fp32 logits [8192,16032]),
+    cross-entropy statistics on those logits, and the embedding gather of
+    8192 ids from a [16032,8192] table.
+Each library call is bracketed by HIP events on the stream it runs on.  One
+JSON line is printed: the headline is the MLP shard's forward+backward
+TFLOP/s; every row's time and throughput is listed under "rows"; "roofline"
+covers the longest single-kernel call (the LM-head GEMM) and "roofline_ce"
+the cross-entropy kernel; "cpu_baseline" times the fp64 oracle on a sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--rows", choices=["all", "mlp"], default="all")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="target CPU time of the oracle sample")
+    return p.parse_args()
+
+
+def src_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "megatron_tensor_layer_tp_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class Row:
+    """One library call of the step, with its algorithmic work per call."""
+
+    def __init__(self, name, config, fn, flops=0.0, bytes_=0.0):
+        self.name, self.config, self.fn = name, config, fn
+        self.flops, self.bytes = flops, bytes_
+        self.events = []
+
+    def run(self, torch, record):
+        if record:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            self.fn()
+            b.record()
+            self.events.append((a, b))
+        else:
+            self.fn()
+
+    def ms(self):
+        return sum(a.elapsed_time(b) for a, b in self.events) / max(1, len(self.events))
+
+
+def build_rows(torch, which):
+    import numpy as np
+
+    from megatron_tensor_layer_tp_amd import inputs as I
+    from megatron_tensor_layer_tp_amd import tpshard as T
+
+    dev = "cuda:0"
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to(dev)
+
+    def bf(shape):
+        return torch.empty(shape, dtype=torch.int16, device=dev)
+
+    BF = T.TP_DT_BF16
+    rows = []
+
+    # ---- MLP shard, GPT-2-small t=2 (the headline workload)
+    d = I.mlp_inputs(2, shards=[0])
+    s, h, ft = d["s"], d["h"], d["ft"]
+    X, W1, W2, dY = up(d["X"]), up(d["W1"][0]), up(d["W2"][0]), up(d["dY"])
+    Z, H, Y = bf((s, ft)), bf((s, ft)), bf((s, h))
+    dX, dW1, dW2 = bf((s, h)), bf((h, ft)), bf((ft, h))
+    nb = T.tp_mlp_bwd_workspace(BF, s, h, ft)
+    ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+    gf = 2.0 * s * h * ft
+    c2 = I.CONFIGS[2]["name"]
+    rows.append(Row("mlp_fwd", c2, lambda: T.tp_mlp_fwd(T.TP_ACT_GELU, BF, s, h, ft, X, W1, W2, Z, H, Y),
+                    flops=2 * gf))
+    rows.append(Row("mlp_bwd", c2, lambda: T.tp_mlp_bwd(T.TP_ACT_GELU, BF, s, h, ft, X, W1, W2, Z, H, dY,
+                                                        dX, dW1, dW2, ws, nb), flops=4 * gf))
+    if which == "mlp":
+        return rows
+
+    # ---- SwiGLU shard and attention projections, Llama-3-70B t=8
+    c4 = I.CONFIGS[4]["name"]
+    sw = I.swiglu_inputs(4)
+    s4, h4, f4 = sw["s"], sw["h"], sw["ft"]
+    X4, dY4 = up(sw["X"]), up(sw["dY"])
+    Wg, Wu, Wd = up(sw["Wg"][0]), up(sw["Wu"][0]), up(sw["Wd"][0])
+    del sw
+    G, U, A = bf((s4, f4)), bf((s4, f4)), bf((s4, f4))
+    Y4, dX4 = bf((s4, h4)), bf((s4, h4))
+    dWg, dWu, dWd = bf((h4, f4)), bf((h4, f4)), bf((f4, h4))
+    nb4 = T.tp_swiglu_bwd_workspace(BF, s4, h4, f4)
+    ws4 = torch.empty(max(nb4, 256), dtype=torch.uint8, device=dev)
+    g4 = 2.0 * s4 * h4 * f4
+    rows.append(Row("swiglu_fwd", c4, lambda: T.tp_swiglu_fwd(BF, s4, h4, f4, X4, Wg, Wu, Wd, G, U, A, Y4),
+                    flops=3 * g4))
+    rows.append(Row("swiglu_bwd", c4, lambda: T.tp_swiglu_bwd(BF, s4, h4, f4, X4, Wg, Wu, Wd, G, U, A, dY4,
+                                                              dX4, dWg, dWu, dWd, ws4, nb4), flops=6 * g4))
+    at = I.attn_inputs(4)
+    dq, dkv = at["dq"], at["dkv"]
+    Wq, Wk, Wv, Wo = (up(at[n][0]) for n in ("Wq", "Wk", "Wv", "Wo"))
+    O, dQ, dK, dV = (up(at[n][0]) for n in ("O", "dQ", "dK", "dV"))
+    del at
+    Q, K, V = bf((s4, dq)), bf((s4, dkv)), bf((s4, dkv))
+    dWq, dWk, dWv, dO, dWo = bf((h4, dq)), bf((h4, dkv)), bf((h4, dkv)), bf((s4, dq)), bf((dq, h4))
+    Ya = bf((s4, h4))
+    nba = T.tp_attn_proj_bwd_workspace(BF, s4, h4, dq, dkv)
+    wsa = torch.empty(max(nba, 256), dtype=torch.uint8, device=dev)
+    qkv = 2.0 * s4 * h4 * (dq + 2 * dkv)
+    og = 2.0 * s4 * dq * h4
+    rows.append(Row("attn_proj_fwd", c4, lambda: T.tp_attn_proj_fwd(BF, s4, h4, dq, dkv, X4, Wq, Wk, Wv, O, Wo,
+                                                                    Q, K, V, Ya), flops=qkv + og))
+    rows.append(Row("attn_proj_bwd", c4, lambda: T.tp_attn_proj_bwd(BF, s4, h4, dq, dkv, X4, Wq, Wk, Wv, O, Wo,
+                                                                    dQ, dK, dV, dY4, dX4, dWq, dWk, dWv, dO,
+                                                                    dWo, wsa, nba), flops=2 * qkv + 2 * og))
+
+    # ---- vocab shard 0, V=128256, t=8
+    c5 = I.CONFIGS[5]["name"]
+    vd = I.vocab_inputs(5, with_logits=False)
+    s5, h5, Vs = vd["s"], vd["h"], vd["Vs"]
+    Hf, Wlm, table = up(vd["Hf"]), up(vd["Wlm"][0]), up(vd["table"][0])
+    tgt, ids = up(vd["targets"]), up(vd["ids"])
+    n_in = int(((vd["ids"] >= 0) & (vd["ids"] < Vs)).sum())
+    del vd
+    logits = torch.empty((s5, Vs), dtype=torch.float32, device=dev)
+    m, se, tl = (torch.empty(s5, dtype=torch.float32, device=dev) for _ in range(3))
+    emb = bf((s5, h5))
+    rows.append(Row("lm_head_fwd", c5, lambda: T.tp_lm_head_fwd(BF, s5, h5, Vs, Hf, Wlm, logits),
+                    flops=2.0 * s5 * h5 * Vs))
+    rows.append(Row("vocab_ce", c5, lambda: T.tp_vocab_ce(s5, Vs, 0, logits, tgt, m, se, tl),
+                    bytes_=4.0 * s5 * Vs + 8.0 * s5 + 12.0 * s5))
+    rows.append(Row("vocab_embed", c5, lambda: T.tp_vocab_embed(BF, s5, Vs, h5, 0, ids, table, emb),
+                    bytes_=2.0 * s5 * h5 + 2.0 * n_in * h5 + 8.0 * s5))
+    return rows
+
+
+def cpu_baseline(seconds: float):
+    """The fp64 oracle's MLP shard forward+backward on the first R rows of the
+    GPT-2-small t=2 shard (full shard weights); R doubles until the sample
+    takes about `seconds`.  Reported as TFLOP/s of the same 6-GEMM count."""
+    import ctypes
+
+    import oracle
+    from megatron_tensor_layer_tp_amd import inputs as I
+
+    oracle.build()
+    d = I.mlp_inputs(2, shards=[0])
+    X = I.bf16_bits_to_f64(d["X"])
+    dY = I.bf16_bits_to_f64(d["dY"])
+    W1 = I.bf16_bits_to_f64(d["W1"][0])
+    W2 = I.bf16_bits_to_f64(d["W2"][0])
+    h, ft = d["h"], d["ft"]
+    R = 256
+    while True:
+        t0 = time.perf_counter()
+        oracle.mlp_fwd("gelu", X[:R], W1, W2)
+        oracle.mlp_bwd("gelu", X[:R], W1, W2, dY[:R])
+        el = time.perf_counter() - t0
+        if el >= seconds / 2 or R >= d["s"]:
+            break
+        R = min(d["s"], R * 2)
+    flops = 6 * 2.0 * R * h * ft
+    try:
+        threads = ctypes.CDLL("libgomp.so.1").omp_get_max_threads()
+    except OSError:
+        threads = None
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"MLP shard fwd+bwd (GeLU), first {R} of {d['s']} rows of the GPT-2-small t=2 "
+                      f"shard, h={h}, f/t={ft}, fp64, {el:.2f} s"}
+
+
+def traffic_for(kernel_key: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when the kernel source changed since the counters were taken."""
+    p = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        t = json.load(f)
+    e = t.get(kernel_key)
+    if not e or e.get("src_hash") != src_hash(*e["sources"]):
+        return None
+    return e["bytes_per_launch"]
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from megatron_tensor_layer_tp_amd import tpshard as T
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    T.lib()  # fails loudly when libtpshard.so is missing
+    torch.cuda.set_device(0)
+    rows = build_rows(torch, args.rows)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        for r in rows:
+            r.run(torch, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for r in rows:
+            r.run(torch, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    by = {r.name: r for r in rows}
+    mlp_ms = by["mlp_fwd"].ms() + by["mlp_bwd"].ms()
+    mlp_flops = by["mlp_fwd"].flops + by["mlp_bwd"].flops
+    value = mlp_flops / (mlp_ms * 1e-3) / 1e12
+    out_rows = {}
+    for r in rows:
+        ms = r.ms()
+        e = {"config": r.config, "ms": round(ms, 4)}
+        if r.flops:
+            tf = r.flops / (ms * 1e-3) / 1e12
+            e.update(tflops=round(tf, 2), frac_mfma_peak=round(tf / PEAK_BF16_TFLOPS, 4))
+        if r.bytes:
+            gbs = r.bytes / (ms * 1e-3) / 1e9
+            e.update(gbs=round(gbs, 1), frac_hbm_peak=round(gbs / PEAK_HBM_GBS, 4))
+        out_rows[r.name] = e
+
+    res = {
+        "metric": "TP-shard MLP fwd+bwd TFLOP/s (bf16, % MFMA peak); vocab-CE GB/s",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,sigma) bf16 inputs, random-init weights)",
+        "config": {"workload": "gpt2-small-gelu-mlp-t2: s=8192 (b=8 x 1024), h=768, f/t=1536, bf16",
+                   "frac_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4),
+                   "step_rows": "mlp fwd+bwd (this workload); swiglu + attention projections fwd+bwd "
+                                "(llama3-70b t=8, s=8192); lm head + vocab CE + embedding "
+                                "(V=128256 t=8, s=8192)" if args.rows == "all" else "mlp fwd+bwd only"},
+        "rows": out_rows,
+    }
+    if "vocab_ce" in by:
+        ce = by["vocab_ce"]
+        res["vocab_ce_gbs"] = out_rows["vocab_ce"]["gbs"]
+    if "lm_head_fwd" in by:
+        r = by["lm_head_fwd"]
+        ach = r.flops / (r.ms() * 1e-3) / 1e12
+        res["roofline"] = {"kernel": "gemm_bf16_kernel<256,256,NN,store fp32> (tp_lm_head_fwd)",
+                           "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
+                           "traffic": traffic_for("lm_head_gemm")}
+        c = by["vocab_ce"]
+        gbs = c.bytes / (c.ms() * 1e-3) / 1e9
+        res["roofline_ce"] = {"kernel": "vocab_ce_kernel<4> (tp_vocab_ce)", "bound": "hbm",
+                              "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                              "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic_for("vocab_ce")}
+    else:
+        r = by["mlp_bwd"]
+        ach = r.flops / (r.ms() * 1e-3) / 1e12
+        res["roofline"] = {"kernel": "gemm_bf16_kernel (tp_mlp_bwd, 4 GEMMs)", "bound": "mfma",
+                           "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()
