@@ -41,6 +41,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--rows", choices=["all", "mlp"], default="all")
+    p.add_argument("--only", default=None,
+                   help="time a single row (e.g. lm_head_fwd) -- for profiling runs")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU time of the oracle sample")
@@ -78,7 +80,7 @@ class Row:
         return sum(a.elapsed_time(b) for a, b in self.events) / max(1, len(self.events))
 
 
-def build_rows(torch, which):
+def build_rows(torch, which, only=None):
     import numpy as np
 
     from megatron_tensor_layer_tp_amd import inputs as I
@@ -98,7 +100,25 @@ def build_rows(torch, which):
     BF = T.TP_DT_BF16
     rows = []
 
+    def want(*names):
+        return only is None or only in names
+
     # ---- MLP shard, GPT-2-small t=2 (the headline workload)
+    if want("mlp_fwd", "mlp_bwd"):
+        rows += mlp_rows(torch, up, bf, I, T)
+    if which == "mlp":
+        return rows
+    if want("swiglu_fwd", "swiglu_bwd", "attn_proj_fwd", "attn_proj_bwd"):
+        rows += layer_rows(torch, up, bf, I, T, want)
+    if want("lm_head_fwd", "vocab_ce", "vocab_embed"):
+        rows += vocab_rows(torch, up, bf, I, T)
+    return rows
+
+
+def mlp_rows(torch, up, bf, I, T):
+    dev = "cuda:0"
+    BF = T.TP_DT_BF16
+    rows = []
     d = I.mlp_inputs(2, shards=[0])
     s, h, ft = d["s"], d["h"], d["ft"]
     X, W1, W2, dY = up(d["X"]), up(d["W1"][0]), up(d["W2"][0]), up(d["dY"])
@@ -112,10 +132,14 @@ def build_rows(torch, which):
                     flops=2 * gf))
     rows.append(Row("mlp_bwd", c2, lambda: T.tp_mlp_bwd(T.TP_ACT_GELU, BF, s, h, ft, X, W1, W2, Z, H, dY,
                                                         dX, dW1, dW2, ws, nb), flops=4 * gf))
-    if which == "mlp":
-        return rows
+    return rows
 
-    # ---- SwiGLU shard and attention projections, Llama-3-70B t=8
+
+def layer_rows(torch, up, bf, I, T, want):
+    """SwiGLU shard and attention projections, Llama-3-70B t=8."""
+    dev = "cuda:0"
+    BF = T.TP_DT_BF16
+    rows = []
     c4 = I.CONFIGS[4]["name"]
     sw = I.swiglu_inputs(4)
     s4, h4, f4 = sw["s"], sw["h"], sw["ft"]
@@ -149,8 +173,14 @@ def build_rows(torch, which):
     rows.append(Row("attn_proj_bwd", c4, lambda: T.tp_attn_proj_bwd(BF, s4, h4, dq, dkv, X4, Wq, Wk, Wv, O, Wo,
                                                                     dQ, dK, dV, dY4, dX4, dWq, dWk, dWv, dO,
                                                                     dWo, wsa, nba), flops=2 * qkv + 2 * og))
+    return rows
 
-    # ---- vocab shard 0, V=128256, t=8
+
+def vocab_rows(torch, up, bf, I, T):
+    """Vocab shard 0 of V=128256, t=8: LM head, CE statistics, embedding."""
+    dev = "cuda:0"
+    BF = T.TP_DT_BF16
+    rows = []
     c5 = I.CONFIGS[5]["name"]
     vd = I.vocab_inputs(5, with_logits=False)
     s5, h5, Vs = vd["s"], vd["h"], vd["Vs"]
@@ -234,7 +264,15 @@ def main():
         sys.exit(1)
     T.lib()  # fails loudly when libtpshard.so is missing
     torch.cuda.set_device(0)
-    rows = build_rows(torch, args.rows)
+    rows = build_rows(torch, args.rows, args.only if args.only != "vocab_ce" else "lm_head_fwd")
+    if args.only:
+        keep = [r for r in rows if r.name == args.only]
+        if not keep:
+            print(f"no row named {args.only}; rows: {[r.name for r in rows]}", file=sys.stderr)
+            sys.exit(2)
+        if args.only == "vocab_ce":  # its input is the LM head's output: compute it once
+            next(r for r in rows if r.name == "lm_head_fwd").fn()
+        rows = keep
     torch.cuda.synchronize()
     for _ in range(args.warmup):
         for r in rows:
@@ -248,6 +286,13 @@ def main():
     wall = time.perf_counter() - t0
 
     by = {r.name: r for r in rows}
+    if args.only:
+        r = rows[0]
+        ms = r.ms()
+        print(json.dumps({"row": r.name, "config": r.config, "ms": ms,
+                          "tflops": r.flops / (ms * 1e-3) / 1e12 if r.flops else None,
+                          "gbs": r.bytes / (ms * 1e-3) / 1e9 if r.bytes else None}))
+        return
     mlp_ms = by["mlp_fwd"].ms() + by["mlp_bwd"].ms()
     mlp_flops = by["mlp_fwd"].flops + by["mlp_bwd"].flops
     value = mlp_flops / (mlp_ms * 1e-3) / 1e12

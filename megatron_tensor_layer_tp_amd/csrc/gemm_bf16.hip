@@ -45,27 +45,61 @@ __device__ __forceinline__ uint32_t elem16(const u32x4 &v, int i) {
   return (i & 1) ? (w >> 16) : (w & 0xffffu);
 }
 
-// Operand tile with k contiguous in memory: R rows x 64 k, R/32 16-byte
-// chunks per thread.  Thread t takes chunk (t & 7) of rows (t >> 3) + 32 i.
+// ---------------------------------------------------------------------------
+// Operand staging.  Every loader has the same interface:
+//   init(ld, extent_left, tid)  per-thread offsets for a new operand / segment
+//   load(tile, kleft, ...)      fetch one 64-deep K slice into registers
+//   store(lds, tid)             write it to LDS as [rows][64 k], swizzled
+// The 16-byte ("VEC") loaders use raw buffer loads: an out-of-range offset
+// returns zeros, so ragged edges need no branches.
+// ---------------------------------------------------------------------------
+constexpr uint32_t OOB = 0x80000000u;       // offset past every buffer's end
+constexpr int NREC = 0x7ffffff0;            // records (bytes) of every buffer
+constexpr int RSRC_W3 = 0x00020000;         // raw buffer, 32-bit data format
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mkrsrc(const void *p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, NREC, RSRC_W3);
+}
+__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+// k-contiguous operand, R rows x 64 k: thread t owns chunk (t & 7) of rows
+// (t >> 3) + 32 i, R/32 chunks.
 template <int R, bool VEC>
 struct LoadKC {
-  u32x4 v[R / 32];
-  __device__ __forceinline__ void load(const uint16_t *p, int64_t ld, int row0, int rows,
-                                       int k0, int klen, int tid) {
-    const int c = tid & 7;
-    const int k = k0 + c * 8;
+  static constexpr int N = R / 32;
+  u32x4 v[N];
+  uint32_t off[N];   // VEC: byte offset of the chunk in the tile, OOB for rows past the edge
+  int64_t ld;
+  int rows_left, c;
+  __device__ __forceinline__ void init(int64_t ld_, int rows_left_, int tid) {
+    ld = ld_;
+    rows_left = rows_left_;
+    c = tid & 7;
 #pragma unroll
-    for (int i = 0; i < R / 32; ++i) {
-      const int row = row0 + (tid >> 3) + 32 * i;
-      if (VEC) {
-        v[i] = (row < rows && k < klen) ? *(const u32x4 *)(p + (int64_t)row * ld + k) : zero4();
-      } else {
+    for (int i = 0; i < N; ++i) {
+      const int rl = (tid >> 3) + 32 * i;
+      off[i] = rl < rows_left ? (uint32_t)(rl * ld * 2 + c * 16) : OOB;
+    }
+  }
+  // tile = &Op[row0][k0]; kleft = valid k from k0 on
+  __device__ __forceinline__ void load(const uint16_t *tile, int kleft, int tid) {
+    if constexpr (VEC) {
+      const __amdgpu_buffer_rsrc_t r = mkrsrc(tile);
+      const bool kok = c * 8 < kleft;
+#pragma unroll
+      for (int i = 0; i < N; ++i) v[i] = bload(r, kok ? off[i] : OOB);
+    } else {
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int rl = (tid >> 3) + 32 * i;
         u32x4 t = zero4();
-        if (row < rows) {
-          const uint16_t *q = p + (int64_t)row * ld;
+        if (rl < rows_left) {
+          const uint16_t *q = tile + (int64_t)rl * ld + c * 8;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            uint32_t x = (k + e < klen) ? q[k + e] : 0u;
+            uint32_t x = (c * 8 + e < kleft) ? q[e] : 0u;
             t[e >> 1] |= (e & 1) ? (x << 16) : x;
           }
         }
@@ -74,44 +108,58 @@ struct LoadKC {
     }
   }
   __device__ __forceinline__ void store(u32x4 *lds, int tid) const {
-    const int c = tid & 7;
 #pragma unroll
-    for (int i = 0; i < R / 32; ++i) {
+    for (int i = 0; i < N; ++i) {
       const int r = (tid >> 3) + 32 * i;
       lds[r * 8 + (c ^ swz(r))] = v[i];
     }
   }
 };
 
-// Operand tile with the row index (m or n) contiguous in memory: the thread
-// owning 8x8 block (kb, rb) loads 8 k-rows of 8 consecutive elements and
-// transposes them so that LDS row rb*8+i holds 8 consecutive k values.
-// Rows >= `half` come from a second matrix p1 (the dual gate/up operand).
-template <int R, bool VEC>
+// Operand with the row index (m or n) contiguous in memory, stored [k][row]:
+// a thread owns one 8x8 block (kb, rb), loads 8 k-rows of 8 consecutive
+// elements and transposes them in registers so that LDS row rb*8+i holds 8
+// consecutive k.  Threads 0-127 cover rows [0, R/2), threads 128-255 rows
+// [R/2, R), so each wave reads from one source: with DUAL the upper half
+// comes from a second matrix (SwiGLU up next to gate) at the same columns.
+template <int R, bool VEC, bool DUAL>
 struct LoadRC {
-  static constexpr int RB = R / 8;  // row blocks
+  static constexpr int H = R / 16;   // row blocks per half
   u32x4 v[8];
-  __device__ __forceinline__ void load(const uint16_t *p0, const uint16_t *p1, int half,
-                                       int64_t ld, int row0, int rows, int k0, int klen,
-                                       int tid) {
-    const int rb = tid % RB, kb = tid / RB;
-    if (kb >= 8) return;
-    int r = rb * 8;
-    const uint16_t *p = p0;
-    if (r >= half) { p = p1; r -= half; }
-    const int col = row0 + r;
+  uint32_t off0;    // VEC: byte offset of (k = 8 kb, col) in the tile, OOB if idle / past the edge
+  uint32_t ld2;
+  int64_t ld;
+  int kb, rb, col, cols_left;
+  bool active;
+  __device__ __forceinline__ void init(int64_t ld_, int cols_left_, int tid) {
+    ld = ld_;
+    ld2 = (uint32_t)(ld_ * 2);
+    cols_left = cols_left_;
+    const int half = tid >> 7, u = tid & 127;
+    rb = half * H + u % H;
+    kb = u / H;
+    active = kb < 8;
+    col = DUAL ? (u % H) * 8 : rb * 8;   // column within the source matrix's tile
+    off0 = (active && col < cols_left) ? (uint32_t)(kb * 8 * ld * 2 + col * 2) : OOB;
+  }
+  // tile = &Op[k0][col0] of this wave's source; kleft = valid k rows from k0
+  __device__ __forceinline__ void load(const uint16_t *tile, int kleft, int tid) {
+    if constexpr (VEC) {
+      const __amdgpu_buffer_rsrc_t r = mkrsrc(tile);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int k = k0 + kb * 8 + e;
-      if (VEC) {
-        v[e] = (k < klen && col < rows) ? *(const u32x4 *)(p + (int64_t)k * ld + col) : zero4();
-      } else {
+      for (int e = 0; e < 8; ++e) {
+        const bool ok = off0 != OOB && kb * 8 + e < kleft;
+        v[e] = bload(r, ok ? off0 + e * ld2 : OOB);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
         u32x4 t = zero4();
-        if (k < klen) {
-          const uint16_t *q = p + (int64_t)k * ld;
+        if (active && kb * 8 + e < kleft) {
+          const uint16_t *q = tile + (int64_t)(kb * 8 + e) * ld + col;
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
-            uint32_t x = (col + i < rows) ? q[col + i] : 0u;
+            uint32_t x = (col + i < cols_left) ? q[i] : 0u;
             t[i >> 1] |= (i & 1) ? (x << 16) : x;
           }
         }
@@ -120,14 +168,12 @@ struct LoadRC {
     }
   }
   __device__ __forceinline__ void store(u32x4 *lds, int tid) const {
-    const int rb = tid % RB, kb = tid / RB;
-    if (kb >= 8) return;
+    if (!active) return;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       u32x4 o;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        o[q] = elem16(v[2 * q], i) | (elem16(v[2 * q + 1], i) << 16);
+      for (int q = 0; q < 4; ++q) o[q] = elem16(v[2 * q], i) | (elem16(v[2 * q + 1], i) << 16);
       const int r = rb * 8 + i;
       lds[r * 8 + (kb ^ swz(r))] = o;
     }
@@ -257,9 +303,11 @@ __device__ __forceinline__ void tile_coords(const GemmDesc &d, int &tm, int &tn,
   tn = w / gsz;
 }
 
-template <int BM, int BN, bool A_KC, bool B_KC, int EPI, bool OUT_F32, bool VEC>
+template <int BM, int BN, bool A_KC, bool B_KC, int EPI, bool OUT_F32, bool VEC, bool KSEG>
 __global__ void __launch_bounds__(NTHREADS) gemm_bf16_kernel(GemmDesc d) {
   __shared__ Smem<BM, BN> sm;
+  constexpr bool DUAL = EPI == EPI_SWIGLU_FWD;
+  static_assert(!(DUAL && (B_KC || KSEG)), "the dual gate/up operand is an n-contiguous weight");
   constexpr int WTM = BM / 2, WTN = BN / 2, FM = WTM / 32, FN = WTN / 32;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
@@ -268,36 +316,63 @@ __global__ void __launch_bounds__(NTHREADS) gemm_bf16_kernel(GemmDesc d) {
   tile_coords(d, tm, tn, split);
 
   int sn = 0;  // N-segment of this tile
-  if (!d.kseg)
+  if constexpr (!KSEG)
     while (sn + 1 < d.nseg && tn >= d.seg_tile0[sn + 1]) ++sn;
-  const int ncols = d.dual ? BN / 2 : BN;
-  const int n0 = d.kseg ? tn * BN : (tn - d.seg_tile0[sn]) * ncols;
-  const int nlen = d.kseg ? d.N : d.seg_len[sn];
+  constexpr int NCOLS = DUAL ? BN / 2 : BN;  // output columns per tile
+  const int n0 = KSEG ? tn * BN : (tn - d.seg_tile0[sn]) * NCOLS;
+  const int nlen = KSEG ? d.N : d.seg_len[sn];
   const int m0 = tm * BM;
 
-  const int kt_total = d.kseg ? d.seg_tile0[d.nseg] : (d.K + BK - 1) / BK;
+  const int kt_total = KSEG ? d.seg_tile0[d.nseg] : (d.K + BK - 1) / BK;
   const int kt_begin = split * d.kt_per_split;
   const int kt_end = min(kt_total, kt_begin + d.kt_per_split);
 
-  typename std::conditional<A_KC, LoadKC<BM, VEC>, LoadRC<BM, VEC>>::type la;
-  typename std::conditional<B_KC, LoadKC<BN, VEC>, LoadRC<BN, VEC>>::type lb;
+  using LA = std::conditional_t<A_KC, LoadKC<BM, VEC>, LoadRC<BM, VEC, false>>;
+  using LB = std::conditional_t<B_KC, LoadKC<BN, VEC>, LoadRC<BN, VEC, DUAL>>;
+  LA la;
+  LB lb;
 
-  auto load_tile = [&](int kt) {
-    int ks = 0;
-    if (d.kseg)
-      while (ks + 1 < d.nseg && kt >= d.seg_tile0[ks + 1]) ++ks;
-    const int k0 = d.kseg ? (kt - d.seg_tile0[ks]) * BK : kt * BK;
-    const int klen = d.kseg ? d.seg_len[ks] : d.K;
-    const int ia = d.kseg ? ks : 0;
-    const int ib = d.kseg ? ks : sn;
-    const uint16_t *Ap = (const uint16_t *)d.A[ia];
-    const uint16_t *Bp = (const uint16_t *)d.B[ib];
-    if constexpr (A_KC) la.load(Ap, d.lda[ia], m0, d.M, k0, klen, tid);
-    else la.load(Ap, Ap, BM, d.lda[ia], m0, d.M, k0, klen, tid);
-    if constexpr (B_KC) lb.load(Bp, d.ldb[ib], n0, nlen, k0, klen, tid);
-    else lb.load(Bp, d.dual ? (const uint16_t *)d.B[1] : Bp, d.dual ? BN / 2 : BN, d.ldb[ib],
-                 n0, nlen, k0, klen, tid);
+  // K cursor: segment ks, offset k0 inside it (segments only with KSEG)
+  int ks = 0, k0;
+  if constexpr (KSEG) {
+    while (ks + 1 < d.nseg && kt_begin >= d.seg_tile0[ks + 1]) ++ks;
+    k0 = (kt_begin - d.seg_tile0[ks]) * BK;
+  } else {
+    k0 = kt_begin * BK;
+  }
+  // the upper half of the workgroup (waves 2, 3) loads the up weight in DUAL mode
+  const int hi = __builtin_amdgcn_readfirstlane(tid >> 7);
+  const uint16_t *Ab, *Bb;
+  int64_t lda, ldb;
+  int klen;
+  auto set_seg = [&]() {
+    const int ia = KSEG ? ks : 0, ib = KSEG ? ks : sn;
+    Ab = (const uint16_t *)d.A[ia];
+    lda = d.lda[ia];
+    Bb = (const uint16_t *)(DUAL ? d.B[hi] : d.B[ib]);
+    ldb = d.ldb[ib];
+    klen = KSEG ? d.seg_len[ks] : d.K;
+    la.init(lda, d.M - m0, tid);
+    lb.init(ldb, nlen - n0, tid);
   };
+  auto fetch = [&]() {
+    const uint16_t *ta = A_KC ? Ab + (int64_t)m0 * lda + k0 : Ab + (int64_t)k0 * lda + m0;
+    const uint16_t *tb = B_KC ? Bb + (int64_t)n0 * ldb + k0 : Bb + (int64_t)k0 * ldb + n0;
+    la.load(ta, klen - k0, tid);
+    lb.load(tb, klen - k0, tid);
+  };
+  auto advance = [&]() {  // only called when another K tile follows
+    k0 += BK;
+    if constexpr (KSEG) {
+      if (k0 >= klen) {
+        k0 = 0;
+        ++ks;
+        while (ks + 1 < d.nseg && d.seg_len[ks] == 0) ++ks;
+        set_seg();
+      }
+    }
+  };
+  set_seg();
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -309,14 +384,13 @@ __global__ void __launch_bounds__(NTHREADS) gemm_bf16_kernel(GemmDesc d) {
 
   // LDS row of the wave's fn-th 32-wide B fragment
   auto brow = [&](int fn) -> int {
-    if (d.dual) {
+    if constexpr (DUAL)
       return (fn < FN / 2) ? wn * (BN / 4) + fn * 32 : BN / 2 + wn * (BN / 4) + (fn - FN / 2) * 32;
-    }
     return wn * WTN + fn * 32;
   };
 
   if (kt_begin < kt_end) {
-    load_tile(kt_begin);
+    fetch();
     la.store(sm.a[0], tid);
     lb.store(sm.b[0], tid);
   }
@@ -325,7 +399,10 @@ __global__ void __launch_bounds__(NTHREADS) gemm_bf16_kernel(GemmDesc d) {
   for (int kt = kt_begin; kt < kt_end; ++kt) {
     const int buf = (kt - kt_begin) & 1;
     const bool more = kt + 1 < kt_end;
-    if (more) load_tile(kt + 1);
+    if (more) {
+      advance();
+      fetch();
+    }
     const u32x4 *As = sm.a[buf];
     const u32x4 *Bs = sm.b[buf];
 #pragma unroll
@@ -364,7 +441,7 @@ __global__ void __launch_bounds__(NTHREADS) gemm_bf16_kernel(GemmDesc d) {
   // 32x32 accumulator layout: element e of lane l is row 8*(e/4) + 4*(l/32) + e%4,
   // column l%32 of the block.
   constexpr int EPS = WTN + 8;                      // strip row stride (floats)
-  constexpr bool DUALE = EPI == EPI_SWIGLU_FWD;
+  constexpr bool DUALE = DUAL;
   constexpr int OUTW = DUALE ? WTN / 2 : WTN;       // output columns per strip row
   constexpr int LPR = OUTW / 8;                     // lanes per strip row
   constexpr int RPI = 64 / LPR;                     // strip rows per pass
@@ -396,7 +473,7 @@ __global__ void __launch_bounds__(NTHREADS) gemm_bf16_kernel(GemmDesc d) {
       const int gm = m0 + wm * WTM + fm * 32 + r;
       const int gn = col_base + c;
       if (gm < d.M && gn < nlen)
-        epi8<EPI, OUT_F32, VEC>(d, gm, gn, nlen, d.kseg ? 0 : sn, split, x, u);
+        epi8<EPI, OUT_F32, VEC>(d, gm, gn, nlen, KSEG ? 0 : sn, split, x, u);
     }
   }
 }
@@ -420,23 +497,33 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmDesc d) {
   }
 }
 
-template <int BM, int BN, bool A_KC, bool B_KC, int EPI, bool OUT_F32, bool VEC>
+template <int BM, int BN, bool A_KC, bool B_KC, int EPI, bool OUT_F32, bool VEC, bool KSEG>
 hipError_t launch_tiles(const GemmDesc &d, hipStream_t st) {
   const int nblk = d.tiles_m * d.tiles_n * d.splits;
   if (nblk == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, A_KC, B_KC, EPI, OUT_F32, VEC>), dim3(nblk),
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, A_KC, B_KC, EPI, OUT_F32, VEC, KSEG>), dim3(nblk),
                      dim3(NTHREADS), 0, st, d);
   return hipGetLastError();
 }
 
+template <bool A_KC, bool B_KC, int EPI, bool OUT_F32, bool KSEG>
+hipError_t launch_shape_k(const GemmDesc &d, int bm, int bn, hipStream_t st, bool vec) {
+  // the scalar-load build exists only for 128x128 tiles (odd sizes are small)
+  if (!vec) return launch_tiles<128, 128, A_KC, B_KC, EPI, OUT_F32, false, KSEG>(d, st);
+  if (bm == 256 && bn == 256) return launch_tiles<256, 256, A_KC, B_KC, EPI, OUT_F32, true, KSEG>(d, st);
+  if (bm == 256 && bn == 128) return launch_tiles<256, 128, A_KC, B_KC, EPI, OUT_F32, true, KSEG>(d, st);
+  if (bm == 128 && bn == 256) return launch_tiles<128, 256, A_KC, B_KC, EPI, OUT_F32, true, KSEG>(d, st);
+  return launch_tiles<128, 128, A_KC, B_KC, EPI, OUT_F32, true, KSEG>(d, st);
+}
+
 template <bool A_KC, bool B_KC, int EPI, bool OUT_F32>
 hipError_t launch_shape(const GemmDesc &d, int bm, int bn, hipStream_t st, bool vec) {
-  // the scalar-load build exists only for 128x128 tiles (odd sizes are small)
-  if (!vec) return launch_tiles<128, 128, A_KC, B_KC, EPI, OUT_F32, false>(d, st);
-  if (bm == 256 && bn == 256) return launch_tiles<256, 256, A_KC, B_KC, EPI, OUT_F32, true>(d, st);
-  if (bm == 256 && bn == 128) return launch_tiles<256, 128, A_KC, B_KC, EPI, OUT_F32, true>(d, st);
-  if (bm == 128 && bn == 256) return launch_tiles<128, 256, A_KC, B_KC, EPI, OUT_F32, true>(d, st);
-  return launch_tiles<128, 128, A_KC, B_KC, EPI, OUT_F32, true>(d, st);
+  // K-segments are used only by the summed dX products (NT, plain store or split-K partial)
+  if constexpr (A_KC && B_KC && (EPI == EPI_STORE || EPI == EPI_PARTIAL)) {
+    if (d.kseg) return launch_shape_k<A_KC, B_KC, EPI, OUT_F32, true>(d, bm, bn, st, vec);
+  }
+  if (d.kseg) return hipErrorInvalidValue;
+  return launch_shape_k<A_KC, B_KC, EPI, OUT_F32, false>(d, bm, bn, st, vec);
 }
 
 }  // namespace
