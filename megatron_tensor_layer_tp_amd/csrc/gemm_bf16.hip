@@ -279,6 +279,55 @@ __device__ __forceinline__ void epi8(const GemmDesc &d, int gm, int gn, int nlen
   }
 }
 
+// ---------------------------------------------------------------------------
+// Epilogue shared by both kernels.  Each wave stages one 32-row strip of its
+// accumulators at a time through LDS (fp32, rows padded by 8 floats so the
+// MFMA-layout writes of the two half-waves fall on different banks), then
+// reads rows back as runs of 8 consecutive columns: the activation math runs
+// once per element and every global access is 16 bytes wide.
+// 32x32 accumulator layout: element e of lane l is row 8*(e/4) + 4*(l/32) + e%4,
+// column l%32 of the block.  `ep` is this wave's private strip (32 x (WTN+8)).
+// All waves of the workgroup must call it (it holds workgroup barriers).
+// ---------------------------------------------------------------------------
+template <int BM, int BN, int EPI, bool OUT_F32, bool VEC, bool DUAL>
+__device__ __forceinline__ void epilogue(const GemmDesc &d, f32x16 (&acc)[BM / 64][BN / 64], float *ep, int lane,
+                                         int wm, int wn, int m0, int n0, int nlen, int sc, int split) {
+  constexpr int WTM = BM / 2, WTN = BN / 2, FM = WTM / 32, FN = WTN / 32;
+  constexpr int EPS = WTN + 8;                      // strip row stride (floats)
+  constexpr int OUTW = DUAL ? WTN / 2 : WTN;        // output columns per strip row
+  constexpr int LPR = OUTW / 8;                     // lanes per strip row
+  constexpr int RPI = 64 / LPR;                     // strip rows per pass
+  const int ci = lane & 31;
+  const int rsub = 4 * (lane >> 5);
+  const int col_base = n0 + (DUAL ? wn * (BN / 4) : wn * WTN);
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    __syncthreads();
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        ep[(8 * (e >> 2) + rsub + (e & 3)) * EPS + fn * 32 + ci] = acc[fm][fn][e];
+    __syncthreads();
+#pragma unroll 2
+    for (int it = 0; it < 32 / RPI; ++it) {
+      const int r = it * RPI + lane / LPR;
+      const int c = (lane % LPR) * 8;
+      const float *src = ep + r * EPS + c;
+      float x[8], u[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) x[q] = src[q];
+      if constexpr (DUAL) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) u[q] = src[OUTW + q];
+      }
+      const int gm = m0 + wm * WTM + fm * 32 + r;
+      const int gn = col_base + c;
+      if (gm < d.M && gn < nlen) epi8<EPI, OUT_F32, VEC>(d, gm, gn, nlen, sc, split, x, u);
+    }
+  }
+}
+
 template <int BM, int BN>
 struct Smem {
   u32x4 a[2][BM * 8];
@@ -432,50 +481,315 @@ __global__ void __launch_bounds__(NTHREADS) gemm_bf16_kernel(GemmDesc d) {
     __syncthreads();
   }
 
-  // ---------------------------------------------------------------- epilogue
-  // Each wave stages one 32-row strip of its accumulators at a time through
-  // LDS (fp32, rows padded by 8 floats so the MFMA-layout writes of the two
-  // half-waves fall on different banks), then reads rows back as runs of 8
-  // consecutive columns: the activation math runs once per element and every
-  // global access is 16 bytes wide.
-  // 32x32 accumulator layout: element e of lane l is row 8*(e/4) + 4*(l/32) + e%4,
-  // column l%32 of the block.
-  constexpr int EPS = WTN + 8;                      // strip row stride (floats)
-  constexpr bool DUALE = DUAL;
-  constexpr int OUTW = DUALE ? WTN / 2 : WTN;       // output columns per strip row
-  constexpr int LPR = OUTW / 8;                     // lanes per strip row
-  constexpr int RPI = 64 / LPR;                     // strip rows per pass
-  float *ep = (float *)&sm + wid * 32 * EPS;
-  const int ci = lane & 31;
-  const int rsub = 4 * (lane >> 5);
-  const int col_base = n0 + (DUALE ? wn * (BN / 4) : wn * WTN);
+  float *ep = (float *)&sm + wid * 32 * (WTN + 8);
+  epilogue<BM, BN, EPI, OUT_F32, VEC, DUAL>(d, acc, ep, lane, wm, wn, m0, n0, nlen, KSEG ? 0 : sn, split);
+}
+
+// ===========================================================================
+// Main kernel: operands move global -> LDS by buffer DMA (no register staging)
+// ===========================================================================
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef short short8v __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) short4v lds_short4v;
+typedef __attribute__((address_space(3))) char lds_char_t;
+
+// k-contiguous tiles [rows][64 k]: 16-byte chunk c of row r sits at c ^ swk(r).
+// Eight consecutive rows hit eight different chunks (conflict-free fragment
+// reads), and the pattern repeats every 32 rows, so fragments 32 rows apart
+// are a fixed byte offset from each other.
+__device__ __forceinline__ int swk(int r) { return (r & 7) ^ ((r >> 3) & 3); }
+// row-contiguous tiles [64 k][C*8]: chunk c of k-row k sits at c ^ swr(k); the
+// 4 k-rows x 32 columns read by half a wave's transpose loads land on 16
+// distinct 16-byte bank groups.
+template <int C>
+__device__ __forceinline__ int swr(int k) { return C >= 16 ? 4 * (k & 3) : 4 * ((k >> 1) & 1); }
+
+// buffer resource words for a wave-uniform base pointer
+__device__ __forceinline__ i32x4 rsrc_words(const void *p) {
+  const uint64_t b = (uint64_t)p;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(b >> 32) & 0xffffu));
+  r[2] = NREC;
+  r[3] = RSRC_W3;
+  return r;
+}
+// 16 bytes per lane from buffer offset voff + soff straight into LDS at
+// lds + 16 * lane.  Issued as asm so that the compiler does not treat the
+// in-flight DMA as an LDS store every later LDS read must wait for (it would
+// wait for the next tile too); the kernel waits on vmcnt explicitly before the
+// barrier that publishes a tile.  The memory clobber keeps LDS accesses in order.
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %3\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(soff), "s"(lds) : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)(const lds_char_t *)p;
+}
+// workgroup barrier without the memory fence of __syncthreads(): the fence
+// would make every wave drain all of its DMA, including the next tile's
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One operand tile (R rows of 64 k, or 64 k-rows of R columns) staged by
+// R/32 one-kilobyte DMA instructions per wave.  DUAL: the R columns are two
+// sub-tiles of R/2 from two matrices; waves 0-1 fill the first, 2-3 the second.
+template <int R, bool KC, bool DUAL>
+struct Dma {
+  static constexpr int NI = R / 32;
+  static constexpr int REFF = DUAL ? R / 2 : R;   // columns of one row-contiguous sub-tile
+  static constexpr int P = 2 * REFF;              // its k-row pitch (bytes)
+  static constexpr int KPB = KC ? 8 : 1024 / P;   // rows / k-rows per kilobyte
+  uint32_t vo[NI];   // per-lane byte offset within the block
+  uint32_t so[NI];   // wave-uniform byte offset of the block
+  int extent;        // rows (KC) or columns (RC) from the tile origin to the matrix edge
+  __device__ __forceinline__ int blk(int wave, int i) const {
+    const int b = wave * NI + i;
+    return (!KC && DUAL) ? b % (REFF / 8) : b;
+  }
+  __device__ __forceinline__ void init(int64_t ld, int extent_, int wave, int lane) {
+    extent = extent_;
 #pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
-    __syncthreads();
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        ep[(8 * (e >> 2) + rsub + (e & 3)) * EPS + fn * 32 + ci] = acc[fm][fn][e];
-    __syncthreads();
-#pragma unroll 2
-    for (int it = 0; it < 32 / RPI; ++it) {
-      const int r = it * RPI + lane / LPR;
-      const int c = (lane % LPR) * 8;
-      const float *src = ep + r * EPS + c;
-      float x[8], u[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) x[q] = src[q];
-      if constexpr (DUALE) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) u[q] = src[OUTW + q];
+    for (int i = 0; i < NI; ++i) {
+      const int bl = blk(wave, i);
+      so[i] = (uint32_t)__builtin_amdgcn_readfirstlane((int)(bl * KPB * ld * 2));
+      if constexpr (KC) {
+        const int r = 8 * bl + (lane >> 3);
+        const int c = (lane & 7) ^ swk(r);
+        vo[i] = (uint32_t)((lane >> 3) * ld * 2 + c * 16);
+      } else {
+        const int k = (bl * 1024 + lane * 16) / P;
+        const int c = ((lane * 16) % P / 16) ^ swr<REFF / 8>(k);
+        vo[i] = (uint32_t)((k - bl * KPB) * ld * 2 + c * 16);
       }
-      const int gm = m0 + wm * WTM + fm * 32 + r;
-      const int gn = col_base + c;
-      if (gm < d.M && gn < nlen)
-        epi8<EPI, OUT_F32, VEC>(d, gm, gn, nlen, KSEG ? 0 : sn, split, x, u);
     }
   }
+  // lane offsets for one K tile (masked on tiles that cross the K or row/column edge)
+  __device__ __forceinline__ void offsets(uint32_t *o, int kleft, int wave, int lane) const {
+    const bool edge = kleft < BK || extent < (KC ? R : REFF);
+#pragma unroll
+    for (int i = 0; i < NI; ++i) o[i] = vo[i];
+    if (edge) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int bl = blk(wave, i);
+        if constexpr (KC) {
+          const int r = 8 * bl + (lane >> 3);
+          const int c = (lane & 7) ^ swk(r);
+          if (r >= extent || c * 8 >= kleft) o[i] = OOB;
+        } else {
+          const int k = (bl * 1024 + lane * 16) / P;
+          const int c = ((lane * 16) % P / 16) ^ swr<REFF / 8>(k);
+          if (k >= kleft || c * 8 >= extent) o[i] = OOB;
+        }
+      }
+    }
+  }
+  __device__ __forceinline__ void issue(const i32x4 &rs, const uint32_t *o, int i, uint32_t region,
+                                        int wave) const {
+    dma16(rs, o[i], so[i], region + (wave * NI + i) * 1024);
+  }
+};
+
+// byte offset (stage-relative) of the first of the two 8-byte transpose reads
+// that give lane l the 4+4 k values of column col0 + l%32 of a row-contiguous
+// sub-tile with pitch P and C chunks per row (h selects the second read)
+__device__ __forceinline__ int rc_frag_off(int P, int C, int col0, int h, int lane) {
+  const int g = (lane >> 4) & 3, j = lane & 15;
+  const int col = col0 + 16 * (g & 1) + 4 * (j & 3);
+  const int k = 8 * (g >> 1) + (j >> 2) + 4 * h;
+  const int sw = C >= 16 ? 4 * (k & 3) : 4 * ((k >> 1) & 1);
+  return k * P + (((col >> 3) ^ sw) << 4) + ((col & 7) << 1);
+}
+__device__ __forceinline__ bf16x8 read_tr(const char *p0, const char *p1) {
+  const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)p0);
+  const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4v *)p1);
+  const short8v v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+template <int BM, int BN, bool A_KC, bool B_KC, int EPI, bool OUT_F32, bool KSEG>
+__global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+gemm_dma_kernel(GemmDesc d) {
+  constexpr int STAGE = 128 * (BM + BN);  // bytes of one A + B tile pair
+  __shared__ __attribute__((aligned(1024))) char smem0[STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem1[STAGE];
+  constexpr bool DUAL = EPI == EPI_SWIGLU_FWD;
+  static_assert(!(DUAL && (B_KC || KSEG)), "the dual gate/up operand is an n-contiguous weight");
+  constexpr int WTM = BM / 2, WTN = BN / 2, FM = WTM / 32, FN = WTN / 32;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wid >> 1, wn = wid & 1;
+
+  int tm, tn, split;
+  tile_coords(d, tm, tn, split);
+  int sn = 0;  // N-segment of this tile
+  if constexpr (!KSEG)
+    while (sn + 1 < d.nseg && tn >= d.seg_tile0[sn + 1]) ++sn;
+  constexpr int NCOLS = DUAL ? BN / 2 : BN;
+  const int n0 = KSEG ? tn * BN : (tn - d.seg_tile0[sn]) * NCOLS;
+  const int nlen = KSEG ? d.N : d.seg_len[sn];
+  const int m0 = tm * BM;
+  const int kt_total = KSEG ? d.seg_tile0[d.nseg] : (d.K + BK - 1) / BK;
+  const int kt_begin = split * d.kt_per_split;
+  const int kt_end = min(kt_total, kt_begin + d.kt_per_split);
+
+  using DA = Dma<BM, A_KC, false>;
+  using DB = Dma<BN, B_KC, DUAL>;
+  constexpr int NLD = DA::NI + DB::NI;  // DMA instructions per wave per tile
+  DA da;
+  DB db;
+
+  // K cursor over the segments: the next tile to stage is (ks, k0)
+  int ks = 0, k0;
+  if constexpr (KSEG) {
+    while (ks + 1 < d.nseg && kt_begin >= d.seg_tile0[ks + 1]) ++ks;
+    k0 = (kt_begin - d.seg_tile0[ks]) * BK;
+  } else {
+    k0 = kt_begin * BK;
+  }
+  const uint16_t *Ab, *Bb;
+  int64_t lda, ldb;
+  int klen;
+  auto set_seg = [&]() {
+    const int ia = KSEG ? ks : 0, ib = KSEG ? ks : sn;
+    Ab = (const uint16_t *)d.A[ia];
+    lda = d.lda[ia];
+    Bb = (const uint16_t *)(DUAL ? d.B[wid >> 1] : d.B[ib]);
+    ldb = d.ldb[ib];
+    klen = KSEG ? d.seg_len[ks] : d.K;
+    da.init(lda, d.M - m0, wid, lane);
+    db.init(ldb, nlen - n0, wid, lane);
+  };
+  set_seg();
+  i32x4 rsa, rsb;
+  uint32_t oa[DA::NI], ob[DB::NI];
+  // descriptors and lane offsets of the tile at the cursor; then advance it
+  auto prep = [&]() {
+    if constexpr (KSEG) {
+      if (k0 >= klen) {
+        k0 = 0;
+        ++ks;
+        while (ks + 1 < d.nseg && d.seg_len[ks] == 0) ++ks;
+        set_seg();
+      }
+    }
+    const uint16_t *ta = A_KC ? Ab + (int64_t)m0 * lda + k0 : Ab + (int64_t)k0 * lda + m0;
+    const uint16_t *tb = B_KC ? Bb + (int64_t)n0 * ldb + k0 : Bb + (int64_t)k0 * ldb + n0;
+    rsa = rsrc_words(ta);
+    rsb = rsrc_words(tb);
+    da.offsets(oa, klen - k0, wid, lane);
+    db.offsets(ob, klen - k0, wid, lane);
+    k0 += BK;
+  };
+  auto dma_q = [&](int q, uint32_t stage) {
+    if (q < DA::NI) da.issue(rsa, oa, q, stage, wid);
+    else db.issue(rsb, ob, q - DA::NI, stage + 128 * BM, wid);
+  };
+
+  // per-lane fragment byte offsets (stage-relative)
+  int aoff[4], boff[4], arc[FM][2], brc[FN][2];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int ra = wm * WTM + (lane & 31);
+    aoff[kk] = ra * 128 + (((kk * 2 + (lane >> 5)) ^ swk(ra)) << 4);
+    const int rb = wn * WTN + (lane & 31);
+    boff[kk] = 128 * BM + rb * 128 + (((kk * 2 + (lane >> 5)) ^ swk(rb)) << 4);
+  }
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) arc[fm][h] = rc_frag_off(2 * BM, BM / 8, wm * WTM + fm * 32, h, lane);
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if constexpr (DUAL)
+        brc[fn][h] = 128 * BM + (fn < FN / 2 ? 0 : 64 * BN) +
+                     rc_frag_off(BN, BN / 16, wn * (BN / 4) + (fn % (FN / 2)) * 32, h, lane);
+      else
+        brc[fn][h] = 128 * BM + rc_frag_off(2 * BN, BN / 8, wn * WTN + fn * 32, h, lane);
+    }
+  auto load_frags = [&](const char *S, int kk, bf16x8 *af, bf16x8 *bfr) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      if constexpr (A_KC) af[fm] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(S + aoff[kk] + fm * 32 * 128));
+      else af[fm] = read_tr(S + arc[fm][0] + kk * 16 * 2 * BM, S + arc[fm][1] + kk * 16 * 2 * BM);
+    }
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      if constexpr (B_KC) {
+        bfr[fn] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(S + boff[kk] + fn * 32 * 128));
+      } else {
+        constexpr int PB = DUAL ? BN : 2 * BN;
+        bfr[fn] = read_tr(S + brc[fn][0] + kk * 16 * PB, S + brc[fn][1] + kk * 16 * PB);
+      }
+    }
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  // One K step on stage S.  The fragments of 16-deep slice kk+1 are read before
+  // the MFMAs of slice kk, and the next tile's DMAs are spread between the MFMA
+  // groups of slices 0 and 1; sched_barrier fences pin both orders.  The single
+  // barrier per step (before it) retired the stage these DMAs overwrite.
+  constexpr int GROUPS = 2 * FM;
+  constexpr int PER = (NLD + GROUPS - 1) / GROUPS;
+  auto step = [&](const char *__restrict__ S, uint32_t nxt, bool more) {
+    bf16x8 fa[2][FM], fb[2][FN];
+    load_frags(S, 0, fa[0], fb[0]);
+    if (more) prep();
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      if (kk < 3) load_frags(S, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][fm], fb[kk & 1][fn], acc[fm][fn], 0, 0, 0);
+        if (kk < 2 && more) {
+          const int g = kk * FM + fm;
+#pragma unroll
+          for (int p = 0; p < PER; ++p)
+            if (g * PER + p < NLD) dma_q(g * PER + p, nxt);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  const uint32_t L0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(smem0));
+  const uint32_t L1 = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(smem1));
+  const int nk = kt_end - kt_begin;
+  if (nk > 0) {
+    prep();
+#pragma unroll
+    for (int q = 0; q < NLD; ++q) dma_q(q, L0);
+  }
+  for (int t = 0; t < nk; ++t) {
+    const char *cur = (t & 1) ? smem1 : smem0;
+    const uint32_t nxt = (t & 1) ? L0 : L1;
+    // this wave's DMA of tile t is the only DMA outstanding here
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+    step(cur, nxt, t + 1 < nk);
+  }
+
+  // epilogue strips: waves 0-1 in stage 0, waves 2-3 in stage 1 (the first
+  // __syncthreads inside the epilogue retires the last tile)
+  float *ep = (float *)(wid < 2 ? smem0 : smem1) + (wid & 1) * 32 * (WTN + 8);
+  epilogue<BM, BN, EPI, OUT_F32, true, DUAL>(d, acc, ep, lane, wm, wn, m0, n0, nlen, KSEG ? 0 : sn, split);
 }
 
 // Sum the split-K partials in split order (deterministic) and store.
@@ -497,23 +811,28 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmDesc d) {
   }
 }
 
-template <int BM, int BN, bool A_KC, bool B_KC, int EPI, bool OUT_F32, bool VEC, bool KSEG>
-hipError_t launch_tiles(const GemmDesc &d, hipStream_t st) {
+template <int BM, int BN, bool A_KC, bool B_KC, int EPI, bool OUT_F32, bool KSEG>
+hipError_t launch_dma(const GemmDesc &d, hipStream_t st) {
   const int nblk = d.tiles_m * d.tiles_n * d.splits;
   if (nblk == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, A_KC, B_KC, EPI, OUT_F32, VEC, KSEG>), dim3(nblk),
-                     dim3(NTHREADS), 0, st, d);
+  hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, A_KC, B_KC, EPI, OUT_F32, KSEG>), dim3(nblk), dim3(NTHREADS), 0, st,
+                     d);
   return hipGetLastError();
 }
 
 template <bool A_KC, bool B_KC, int EPI, bool OUT_F32, bool KSEG>
 hipError_t launch_shape_k(const GemmDesc &d, int bm, int bn, hipStream_t st, bool vec) {
-  // the scalar-load build exists only for 128x128 tiles (odd sizes are small)
-  if (!vec) return launch_tiles<128, 128, A_KC, B_KC, EPI, OUT_F32, false, KSEG>(d, st);
-  if (bm == 256 && bn == 256) return launch_tiles<256, 256, A_KC, B_KC, EPI, OUT_F32, true, KSEG>(d, st);
-  if (bm == 256 && bn == 128) return launch_tiles<256, 128, A_KC, B_KC, EPI, OUT_F32, true, KSEG>(d, st);
-  if (bm == 128 && bn == 256) return launch_tiles<128, 256, A_KC, B_KC, EPI, OUT_F32, true, KSEG>(d, st);
-  return launch_tiles<128, 128, A_KC, B_KC, EPI, OUT_F32, true, KSEG>(d, st);
+  if (!vec) {  // element-wise loads (odd sizes / leading dimensions): 128x128 tiles only
+    const int nblk = d.tiles_m * d.tiles_n * d.splits;
+    if (nblk == 0) return hipSuccess;
+    hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, A_KC, B_KC, EPI, OUT_F32, false, KSEG>), dim3(nblk),
+                       dim3(NTHREADS), 0, st, d);
+    return hipGetLastError();
+  }
+  if (bm == 256 && bn == 256) return launch_dma<256, 256, A_KC, B_KC, EPI, OUT_F32, KSEG>(d, st);
+  if (bm == 256 && bn == 128) return launch_dma<256, 128, A_KC, B_KC, EPI, OUT_F32, KSEG>(d, st);
+  if (bm == 128 && bn == 256) return launch_dma<128, 256, A_KC, B_KC, EPI, OUT_F32, KSEG>(d, st);
+  return launch_dma<128, 128, A_KC, B_KC, EPI, OUT_F32, KSEG>(d, st);
 }
 
 template <bool A_KC, bool B_KC, int EPI, bool OUT_F32>

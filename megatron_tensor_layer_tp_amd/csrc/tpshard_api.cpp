@@ -150,7 +150,9 @@ double tile_eff(int bm, int bn) {
 Plan plan_bf16(const Spec &s) {
   Plan p;
   bool vec = true;
-  for (int i = 0; i < s.nlds; ++i) vec &= s.lds[i] % 8 == 0;
+  // 16-byte DMA / buffer loads: leading dimensions multiples of 8 elements, and
+  // a 256-row tile's byte span addressable with 32-bit buffer offsets
+  for (int i = 0; i < s.nlds; ++i) vec &= s.lds[i] % 8 == 0 && s.lds[i] < (int64_t(1) << 21);
   vec &= s.M % 8 == 0;
   if (s.kseg) {
     vec &= s.N % 8 == 0;
