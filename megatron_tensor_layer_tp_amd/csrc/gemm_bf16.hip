@@ -182,10 +182,16 @@ struct LoadRC {
 
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+// 8 fp32 -> 8 bf16 with the hardware pair conversion (round to nearest even)
 __device__ __forceinline__ u32x4 pack8(const float *v) {
   u32x4 o;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) o[q] = (uint32_t)tp_f2bf(v[2 * q]) | ((uint32_t)tp_f2bf(v[2 * q + 1]) << 16);
+  for (int q = 0; q < 4; ++q) {
+    const f32x2_t p = {v[2 * q], v[2 * q + 1]};
+    o[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2_t));
+  }
   return o;
 }
 
@@ -792,22 +798,49 @@ gemm_dma_kernel(GemmDesc d) {
   epilogue<BM, BN, EPI, OUT_F32, true, DUAL>(d, acc, ep, lane, wm, wn, m0, n0, nlen, KSEG ? 0 : sn, split);
 }
 
-// Sum the split-K partials in split order (deterministic) and store.
-template <bool OUT_F32>
+// Sum the split-K partials in split order (deterministic) and store.  Each
+// thread owns a run of 8 columns of one row (VEC: N and the segment widths
+// are multiples of 8); the scalar build owns single elements.
+template <bool OUT_F32, bool VEC>
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmDesc d) {
-  const int64_t total = (int64_t)d.M * d.N;
+  constexpr int W = VEC ? 8 : 1;
+  const int runs = d.N / W;
+  const int64_t total = (int64_t)d.M * runs;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {
-    const int gm = (int)(i / d.N), gc = (int)(i - (int64_t)gm * d.N);
-    float s = 0.f;
-    for (int k = 0; k < d.splits; ++k) s += d.ws[((int64_t)k * d.M + gm) * d.N + gc];
+    const int gm = (int)(i / runs);
+    const int gc = (int)(i - (int64_t)gm * runs) * W;
+    float s[W];
+#pragma unroll
+    for (int q = 0; q < W; ++q) s[q] = 0.f;
+    for (int k = 0; k < d.splits; ++k) {
+      const float *p = d.ws + ((int64_t)k * d.M + gm) * d.N + gc;
+      if constexpr (VEC) {
+        const float4 a = *(const float4 *)p, b = *(const float4 *)(p + 4);
+        s[0] += a.x; s[1] += a.y; s[2] += a.z; s[3] += a.w;
+        s[4] += b.x; s[5] += b.y; s[6] += b.z; s[7] += b.w;
+      } else {
+        s[0] += p[0];
+      }
+    }
     int sg = 0;
     if (!d.kseg)
       while (sg + 1 < d.nseg && gc >= d.seg_col0[sg + 1]) ++sg;
     const int cc = d.kseg ? gc : gc - d.seg_col0[sg];
     const int si = d.kseg ? 0 : sg;
-    if (OUT_F32) ((float *)d.C[si])[(int64_t)gm * d.ldc[si] + cc] = s;
-    else ((uint16_t *)d.C[si])[(int64_t)gm * d.ldc[si] + cc] = tp_f2bf(s);
+    if constexpr (OUT_F32) {
+      float *o = (float *)d.C[si] + (int64_t)gm * d.ldc[si] + cc;
+      if constexpr (VEC) {
+        *(float4 *)o = make_float4(s[0], s[1], s[2], s[3]);
+        *(float4 *)(o + 4) = make_float4(s[4], s[5], s[6], s[7]);
+      } else {
+        o[0] = s[0];
+      }
+    } else {
+      uint16_t *o = (uint16_t *)d.C[si] + (int64_t)gm * d.ldc[si] + cc;
+      if constexpr (VEC) *(u32x4 *)o = pack8(s);
+      else o[0] = tp_f2bf(s[0]);
+    }
   }
 }
 
@@ -886,12 +919,15 @@ hipError_t tp_launch_gemm_bf16(const GemmDesc &d, int layout, int epi, bool out_
   return e;
 }
 
-hipError_t tp_launch_splitk_reduce(const GemmDesc &d, bool out_f32, hipStream_t st) {
-  const int64_t total = (int64_t)d.M * d.N;
+hipError_t tp_launch_splitk_reduce(const GemmDesc &d, bool out_f32, bool vec, hipStream_t st) {
+  const int64_t total = (int64_t)d.M * (vec ? d.N / 8 : d.N);
   if (total == 0) return hipSuccess;
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  if (out_f32) hipLaunchKernelGGL(splitk_reduce_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, st, d);
-  else hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, st, d);
+  const dim3 g((unsigned)blocks), b(256);
+  if (out_f32 && vec) hipLaunchKernelGGL((splitk_reduce_kernel<true, true>), g, b, 0, st, d);
+  else if (out_f32) hipLaunchKernelGGL((splitk_reduce_kernel<true, false>), g, b, 0, st, d);
+  else if (vec) hipLaunchKernelGGL((splitk_reduce_kernel<false, true>), g, b, 0, st, d);
+  else hipLaunchKernelGGL((splitk_reduce_kernel<false, false>), g, b, 0, st, d);
   return hipGetLastError();
 }

@@ -62,21 +62,44 @@ struct GemmDesc {
 #if defined(__HIPCC__)
 #include <hip/hip_runtime.h>
 
+// Element-wise activations, evaluated in fp32 with the hardware exp2 / rcp.
+// erf comes from Abramowitz & Stegun, Handbook of Mathematical Functions,
+// formula 7.1.26 (Hastings): erf(x) = 1 - t (a1 + t (a2 + ... + t a5)) e^{-x^2},
+// t = 1 / (1 + p |x|), |error| <= 1.5e-7 -- far below bf16's 2^-9 resolution.
+// For GeLU the same e^{-z^2/2} serves Phi(z) = (1 + erf(z/sqrt 2)) / 2 and the
+// normal density phi(z) = e^{-z^2/2} / sqrt(2 pi) of its derivative.
+__device__ __forceinline__ float tp_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float tp_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// Phi(z) given e = exp(-z*z/2)
+__device__ __forceinline__ float tp_phi_cdf(float z, float e) {
+  const float ax = fabsf(z) * 0.70710678118654752f;
+  const float t = tp_rcp(fmaf(0.3275911f, ax, 1.f));
+  float p = fmaf(1.061405429f, t, -1.453152027f);
+  p = fmaf(p, t, 1.421413741f);
+  p = fmaf(p, t, -0.284496736f);
+  p = fmaf(p, t, 0.254829592f);
+  const float erf_ax = fmaf(-p * t, e, 1.f);
+  return 0.5f + 0.5f * copysignf(erf_ax, z);
+}
+__device__ __forceinline__ float tp_gauss(float z) {  // exp(-z^2 / 2)
+  return tp_exp2(-0.72134752044448170f * z * z);     // log2(e) / 2
+}
+
 __device__ __forceinline__ float tp_act_fwd(int act, float z) {
   if (act == ACT_RELU) return z > 0.f ? z : 0.f;
-  // GeLU, exact form z * Phi(z)
-  return 0.5f * z * (1.f + erff(z * 0.70710678118654752f));
+  return z * tp_phi_cdf(z, tp_gauss(z));  // GeLU, exact form z * Phi(z)
 }
 
 __device__ __forceinline__ float tp_act_grad(int act, float z) {
   if (act == ACT_RELU) return z > 0.f ? 1.f : 0.f;
-  // d/dz z*Phi(z) = Phi(z) + z*phi(z)
-  float Phi = 0.5f * (1.f + erff(z * 0.70710678118654752f));
-  float phi = 0.39894228040143268f * expf(-0.5f * z * z);
-  return fmaf(z, phi, Phi);
+  const float e = tp_gauss(z);
+  return fmaf(z * 0.39894228040143268f, e, tp_phi_cdf(z, e));  // Phi(z) + z phi(z)
 }
 
-__device__ __forceinline__ float tp_sigmoid(float z) { return 1.f / (1.f + expf(-z)); }
+__device__ __forceinline__ float tp_sigmoid(float z) {
+  return tp_rcp(1.f + tp_exp2(-1.4426950408889634f * z));
+}
 
 // round-to-nearest-even fp32 -> bfloat16 bits
 __device__ __forceinline__ uint16_t tp_f2bf(float f) {

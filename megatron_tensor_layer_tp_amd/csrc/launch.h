@@ -14,7 +14,7 @@ enum GemmLayout : int {
 // every operand (aligned pointers, leading dimensions and extents multiple of 8).
 hipError_t tp_launch_gemm_bf16(const GemmDesc &d, int layout, int epi, bool out_f32, int bm, int bn,
                                bool vec, hipStream_t st);
-hipError_t tp_launch_splitk_reduce(const GemmDesc &d, bool out_f32, hipStream_t st);
+hipError_t tp_launch_splitk_reduce(const GemmDesc &d, bool out_f32, bool vec, hipStream_t st);
 
 // fp32 storage and arithmetic (64x64 tiles, any layout, any extents).
 constexpr int TP_F32_TILE = 64;
