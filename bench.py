@@ -44,6 +44,8 @@ def parse():
     p.add_argument("--only", default=None,
                    help="time a single row (e.g. lm_head_fwd) -- for profiling runs")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a 1 GiB device-to-device copy (HBM counter calibration)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU time of the oracle sample")
     return p.parse_args()
@@ -264,6 +266,15 @@ def main():
         sys.exit(1)
     T.lib()  # fails loudly when libtpshard.so is missing
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        # a plain copy of known size: reads and writes exactly 1 GiB per launch
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": 1 << 30, "launches": 3}))
+        return
     rows = build_rows(torch, args.rows, args.only if args.only != "vocab_ce" else "lm_head_fwd")
     if args.only:
         keep = [r for r in rows if r.name == args.only]
