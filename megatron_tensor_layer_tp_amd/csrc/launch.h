@@ -16,6 +16,18 @@ hipError_t tp_launch_gemm_bf16(const GemmDesc &d, int layout, int epi, bool out_
                                bool vec, hipStream_t st);
 hipError_t tp_launch_splitk_reduce(const GemmDesc &d, bool out_f32, bool vec, hipStream_t st);
 
+// Two independent bf16 products in one launch (the second must not be split).
+// With dry = true nothing is launched: the return value only says whether the
+// pair of variants is built (hipSuccess) or not (hipErrorNotSupported).
+struct GemmVariant {
+  int layout, epi;
+  bool out_f32;
+  int bm, bn;
+  bool vec;
+};
+hipError_t tp_launch_gemm_pair(const GemmDesc &d1, const GemmVariant &v1, const GemmDesc &d2,
+                               const GemmVariant &v2, bool dry, hipStream_t st);
+
 // fp32 storage and arithmetic (64x64 tiles, any layout, any extents).
 constexpr int TP_F32_TILE = 64;
 hipError_t tp_launch_gemm_f32(const GemmDesc &d, int layout, int epi, hipStream_t st);

@@ -115,6 +115,7 @@ struct Spec {               // one product, described before planning
   bool kseg = false;
   bool dual = false;
   bool can_split = false;   // a workspace for split-K partials is available
+  bool bm256 = false;       // only 256-row tiles (the shapes built for paired launches)
   int64_t seg[TP_MAX_SEG] = {0, 0, 0};  // N-extents (N-segments) or K-extents (K-segments)
   int64_t N = 0;            // total N (kseg or single segment)
   int64_t lds[12] = {};     // every leading dimension involved
@@ -169,6 +170,7 @@ Plan plan_bf16(const Spec &s) {
   for (auto &sh : shapes) {
     const int bm = sh[0], bn = sh[1];
     if (!vec && !(bm == 128 && bn == 128)) continue;
+    if (s.bm256 && bm != 256) continue;
     const int64_t tm = cdiv(s.M, bm), tn = ntiles_n(s, bn);
     const int64_t tiles = tm * tn;
     const int slots = (bm == 128 && bn == 128) ? 2 * kCUs : kCUs;
@@ -234,8 +236,7 @@ struct Ptrs {
   int act = ACT_RELU;
 };
 
-int run(const Spec &s, const Ptrs &q, int dt, void *ws, hipStream_t st, const char *what) {
-  const Plan p = plan(s, dt);
+GemmDesc make_desc(const Spec &s, const Ptrs &q, const Plan &p, int dt, void *ws) {
   GemmDesc d;
   std::memset(&d, 0, sizeof d);
   d.M = (int32_t)s.M;
@@ -275,17 +276,92 @@ int run(const Spec &s, const Ptrs &q, int dt, void *ws, hipStream_t st, const ch
   d.tiles_n = p.tiles_n;
   d.group_m = 8;
   d.ws = (float *)ws;
+  return d;
+}
+
+// the kernel variant a bf16 plan launches (split-K plans write fp32 partials)
+GemmVariant variant(const Spec &s, const Plan &p) {
+  GemmVariant v;
+  v.layout = s.layout;
+  v.epi = p.splits > 1 ? (int)EPI_PARTIAL : s.epi;
+  v.out_f32 = p.splits > 1 ? true : s.out_f32;
+  v.bm = p.bm;
+  v.bn = p.bn;
+  v.vec = p.vec;
+  return v;
+}
+
+int run_planned(const Spec &s, const Plan &p, const Ptrs &q, int dt, void *ws, hipStream_t st,
+                const char *what) {
   if (p.splits > 1 && ws == nullptr) return fail(TP_EWORKSPACE, "%s: split-K plan without workspace", what);
+  const GemmDesc d = make_desc(s, q, p, dt, ws);
   hipError_t e;
   if (dt == TP_DT_F32) {
     e = tp_launch_gemm_f32(d, s.layout, s.epi, st);
-  } else if (p.splits > 1) {
-    e = tp_launch_gemm_bf16(d, s.layout, EPI_PARTIAL, true, p.bm, p.bn, p.vec, st);
-    if (e == hipSuccess) e = tp_launch_splitk_reduce(d, s.out_f32, p.vec, st);
   } else {
-    e = tp_launch_gemm_bf16(d, s.layout, s.epi, s.out_f32, p.bm, p.bn, p.vec, st);
+    const GemmVariant v = variant(s, p);
+    e = tp_launch_gemm_bf16(d, v.layout, v.epi, v.out_f32, p.bm, p.bn, p.vec, st);
+    if (e == hipSuccess && p.splits > 1) e = tp_launch_splitk_reduce(d, s.out_f32, p.vec, st);
   }
   if (e != hipSuccess) return fail(TP_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return TP_OK;
+}
+
+int run(const Spec &s, const Ptrs &q, int dt, void *ws, hipStream_t st, const char *what) {
+  return run_planned(s, plan(s, dt), q, dt, ws, st, what);
+}
+
+// Two independent products of one pass.  In bf16 they share one launch when
+// both plans fit the paired kernels: the first (long-K) product may be split
+// along K, the second is not.  Otherwise they run one after the other with
+// their own plans.  Plans depend on the sizes alone, so the workspace queries
+// see the same ones.
+struct PairPlan {
+  bool paired = false;
+  Plan p1, p2;
+};
+
+PairPlan pair_plan(const Spec &s1, const Spec &s2, int dt) {
+  PairPlan r;
+  if (dt == TP_DT_BF16) {
+    Spec a = s1, b = s2;
+    a.bm256 = b.bm256 = true;
+    b.can_split = false;
+    r.p1 = plan_bf16(a);
+    r.p2 = plan_bf16(b);
+    GemmDesc d1, d2;
+    std::memset(&d1, 0, sizeof d1);
+    std::memset(&d2, 0, sizeof d2);
+    d1.kseg = a.kseg;
+    d2.kseg = b.kseg;
+    r.paired = r.p1.vec && r.p2.vec &&
+               tp_launch_gemm_pair(d1, variant(a, r.p1), d2, variant(b, r.p2), true, nullptr) == hipSuccess;
+  }
+  if (!r.paired) {
+    r.p1 = plan(s1, dt);
+    r.p2 = plan(s2, dt);
+  }
+  return r;
+}
+
+size_t pair_ws_bytes(const Spec &s1, const Spec &s2, int dt) {
+  const PairPlan pp = pair_plan(s1, s2, dt);
+  return std::max(align256(pp.p1.ws_bytes), align256(pp.p2.ws_bytes));
+}
+
+int run_pair(const Spec &s1, const Ptrs &q1, const Spec &s2, const Ptrs &q2, int dt, void *ws, hipStream_t st,
+             const char *what1, const char *what2) {
+  const PairPlan pp = pair_plan(s1, s2, dt);
+  if (!pp.paired) {
+    if (int e = run_planned(s1, pp.p1, q1, dt, ws, st, what1)) return e;
+    return run_planned(s2, pp.p2, q2, dt, ws, st, what2);
+  }
+  if (pp.p1.splits > 1 && ws == nullptr) return fail(TP_EWORKSPACE, "%s: split-K plan without workspace", what1);
+  const GemmDesc d1 = make_desc(s1, q1, pp.p1, dt, ws);
+  const GemmDesc d2 = make_desc(s2, q2, pp.p2, dt, nullptr);
+  hipError_t e = tp_launch_gemm_pair(d1, variant(s1, pp.p1), d2, variant(s2, pp.p2), false, st);
+  if (e == hipSuccess && pp.p1.splits > 1) e = tp_launch_splitk_reduce(d1, s1.out_f32, pp.p1.vec, st);
+  if (e != hipSuccess) return fail(TP_EHIP, "%s + %s: %s", what1, what2, hipGetErrorString(e));
   return TP_OK;
 }
 
@@ -337,8 +413,7 @@ MlpBwdLayout mlp_bwd_layout(int dt, int64_t s, int64_t h, int64_t ft) {
   L.g_dw1 = spec_tn(h, ft, s);
   for (Spec *g : {&L.g_dz, &L.g_dw2, &L.g_dx, &L.g_dw1}) g->can_split = true;
   L.dz_bytes = align256((size_t)s * ft * esize(dt));
-  for (const Spec *g : {&L.g_dz, &L.g_dw2, &L.g_dx, &L.g_dw1})
-    L.part_bytes = std::max(L.part_bytes, align256(plan(*g, dt).ws_bytes));
+  L.part_bytes = std::max(pair_ws_bytes(L.g_dw2, L.g_dz, dt), pair_ws_bytes(L.g_dw1, L.g_dx, dt));
   L.total = L.dz_bytes + L.part_bytes;
   return L;
 }
@@ -378,8 +453,7 @@ SwigluBwdLayout swiglu_bwd_layout(int dt, int64_t s, int64_t h, int64_t ft) {
   L.g_dwgu = dw;
   for (Spec *g : {&L.g_da, &L.g_dwd, &L.g_dx, &L.g_dwgu}) g->can_split = true;
   L.dg_bytes = align256((size_t)s * ft * esize(dt));
-  for (const Spec *g : {&L.g_da, &L.g_dwd, &L.g_dx, &L.g_dwgu})
-    L.part_bytes = std::max(L.part_bytes, align256(plan(*g, dt).ws_bytes));
+  L.part_bytes = std::max(pair_ws_bytes(L.g_dwd, L.g_da, dt), pair_ws_bytes(L.g_dwgu, L.g_dx, dt));
   L.total = 2 * L.dg_bytes + L.part_bytes;
   return L;
 }
@@ -420,8 +494,7 @@ AttnBwdLayout attn_bwd_layout(int dt, int64_t s, int64_t h, int64_t dq, int64_t 
   L.g_do = spec_nt(s, dq, h, EPI_STORE);
   L.g_dwo = spec_tn(dq, h, s);
   for (Spec *g : {&L.g_dx, &L.g_dwqkv, &L.g_do, &L.g_dwo}) g->can_split = true;
-  for (const Spec *g : {&L.g_dx, &L.g_dwqkv, &L.g_do, &L.g_dwo})
-    L.part_bytes = std::max(L.part_bytes, align256(plan(*g, dt).ws_bytes));
+  L.part_bytes = std::max(pair_ws_bytes(L.g_dwqkv, L.g_dx, dt), pair_ws_bytes(L.g_dwo, L.g_do, dt));
   L.total = L.part_bytes;
   return L;
 }
@@ -524,35 +597,31 @@ int tp_mlp_bwd(int act, int dt, int64_t s, int64_t h, int64_t ft, const void *X,
   void *dZ = wsb;
   void *part = wsb + L.dz_bytes;
   const int a = act == TP_ACT_GELU ? ACT_GELU : ACT_RELU;
-  {  // dZ = (dY . W2^T) * act'(Z)   (ReLU mask from Z, or from H when Z is absent)
-    Ptrs p;
-    p.A[0] = dY; p.lda[0] = h;
-    p.B[0] = W2; p.ldb[0] = h;
-    p.C[0] = dZ; p.ldc[0] = ft;
-    p.ai0 = Z ? Z : H; p.ldai = ft;
-    p.act = a;
-    if (int e = run(L.g_dz, p, dt, part, st, "tp_mlp_bwd dZ GEMM")) return e;
+  {  // dW2 = H^T . dY  beside  dZ = (dY . W2^T) * act'(Z)  (ReLU mask from Z, or from H without Z)
+    Ptrs pw;
+    pw.A[0] = H; pw.lda[0] = ft;
+    pw.B[0] = dY; pw.ldb[0] = h;
+    pw.C[0] = dW2; pw.ldc[0] = h;
+    Ptrs pz;
+    pz.A[0] = dY; pz.lda[0] = h;
+    pz.B[0] = W2; pz.ldb[0] = h;
+    pz.C[0] = dZ; pz.ldc[0] = ft;
+    pz.ai0 = Z ? Z : H; pz.ldai = ft;
+    pz.act = a;
+    if (int e = run_pair(L.g_dw2, pw, L.g_dz, pz, dt, part, st, "tp_mlp_bwd dW2 GEMM", "tp_mlp_bwd dZ GEMM"))
+      return e;
   }
-  {  // dW2 = H^T . dY
-    Ptrs p;
-    p.A[0] = H; p.lda[0] = ft;
-    p.B[0] = dY; p.ldb[0] = h;
-    p.C[0] = dW2; p.ldc[0] = h;
-    if (int e = run(L.g_dw2, p, dt, part, st, "tp_mlp_bwd dW2 GEMM")) return e;
-  }
-  {  // dX = dZ . W1^T
-    Ptrs p;
-    p.A[0] = dZ; p.lda[0] = ft;
-    p.B[0] = W1; p.ldb[0] = ft;
-    p.C[0] = dX; p.ldc[0] = h;
-    if (int e = run(L.g_dx, p, dt, part, st, "tp_mlp_bwd dX GEMM")) return e;
-  }
-  {  // dW1 = X^T . dZ
-    Ptrs p;
-    p.A[0] = X; p.lda[0] = h;
-    p.B[0] = dZ; p.ldb[0] = ft;
-    p.C[0] = dW1; p.ldc[0] = ft;
-    if (int e = run(L.g_dw1, p, dt, part, st, "tp_mlp_bwd dW1 GEMM")) return e;
+  {  // dW1 = X^T . dZ  beside  dX = dZ . W1^T
+    Ptrs pw;
+    pw.A[0] = X; pw.lda[0] = h;
+    pw.B[0] = dZ; pw.ldb[0] = ft;
+    pw.C[0] = dW1; pw.ldc[0] = ft;
+    Ptrs px;
+    px.A[0] = dZ; px.lda[0] = ft;
+    px.B[0] = W1; px.ldb[0] = ft;
+    px.C[0] = dX; px.ldc[0] = h;
+    if (int e = run_pair(L.g_dw1, pw, L.g_dx, px, dt, part, st, "tp_mlp_bwd dW1 GEMM", "tp_mlp_bwd dX GEMM"))
+      return e;
   }
   return ok();
 }
@@ -616,35 +685,32 @@ int tp_swiglu_bwd(int dt, int64_t s, int64_t h, int64_t ft, const void *X, const
   hipStream_t st = (hipStream_t)stream;
   char *wsb = (char *)ws;
   void *dG = wsb, *dU = wsb + L.dg_bytes, *part = wsb + 2 * L.dg_bytes;
-  {  // dA = dY . Wd^T;  dG = dA * U * SiLU'(G);  dU = dA * SiLU(G)
-    Ptrs p;
-    p.A[0] = dY; p.lda[0] = h;
-    p.B[0] = Wd; p.ldb[0] = h;
-    p.C[0] = dG; p.ldc[0] = ft;
-    p.ai0 = G; p.ai1 = U; p.ldai = ft;
-    p.ao0 = dU; p.ldao = ft;
-    if (int e = run(L.g_da, p, dt, part, st, "tp_swiglu_bwd dA GEMM")) return e;
+  {  // dWd = A^T . dY  beside  dA = dY . Wd^T, dG = dA * U * SiLU'(G), dU = dA * SiLU(G)
+    Ptrs pw;
+    pw.A[0] = A; pw.lda[0] = ft;
+    pw.B[0] = dY; pw.ldb[0] = h;
+    pw.C[0] = dWd; pw.ldc[0] = h;
+    Ptrs pa;
+    pa.A[0] = dY; pa.lda[0] = h;
+    pa.B[0] = Wd; pa.ldb[0] = h;
+    pa.C[0] = dG; pa.ldc[0] = ft;
+    pa.ai0 = G; pa.ai1 = U; pa.ldai = ft;
+    pa.ao0 = dU; pa.ldao = ft;
+    if (int e = run_pair(L.g_dwd, pw, L.g_da, pa, dt, part, st, "tp_swiglu_bwd dWd GEMM", "tp_swiglu_bwd dA GEMM"))
+      return e;
   }
-  {  // dWd = A^T . dY
-    Ptrs p;
-    p.A[0] = A; p.lda[0] = ft;
-    p.B[0] = dY; p.ldb[0] = h;
-    p.C[0] = dWd; p.ldc[0] = h;
-    if (int e = run(L.g_dwd, p, dt, part, st, "tp_swiglu_bwd dWd GEMM")) return e;
-  }
-  {  // dX = dG . Wg^T + dU . Wu^T
-    Ptrs p;
-    p.A[0] = dG; p.A[1] = dU; p.lda[0] = p.lda[1] = ft;
-    p.B[0] = Wg; p.B[1] = Wu; p.ldb[0] = p.ldb[1] = ft;
-    p.C[0] = dX; p.ldc[0] = h;
-    if (int e = run(L.g_dx, p, dt, part, st, "tp_swiglu_bwd dX GEMM")) return e;
-  }
-  {  // [dWg | dWu] = X^T . [dG | dU]
-    Ptrs p;
-    p.A[0] = X; p.lda[0] = h;
-    p.B[0] = dG; p.B[1] = dU; p.ldb[0] = p.ldb[1] = ft;
-    p.C[0] = dWg; p.C[1] = dWu; p.ldc[0] = p.ldc[1] = ft;
-    if (int e = run(L.g_dwgu, p, dt, part, st, "tp_swiglu_bwd dWg/dWu GEMM")) return e;
+  {  // [dWg | dWu] = X^T . [dG | dU]  beside  dX = dG . Wg^T + dU . Wu^T
+    Ptrs pw;
+    pw.A[0] = X; pw.lda[0] = h;
+    pw.B[0] = dG; pw.B[1] = dU; pw.ldb[0] = pw.ldb[1] = ft;
+    pw.C[0] = dWg; pw.C[1] = dWu; pw.ldc[0] = pw.ldc[1] = ft;
+    Ptrs px;
+    px.A[0] = dG; px.A[1] = dU; px.lda[0] = px.lda[1] = ft;
+    px.B[0] = Wg; px.B[1] = Wu; px.ldb[0] = px.ldb[1] = ft;
+    px.C[0] = dX; px.ldc[0] = h;
+    if (int e = run_pair(L.g_dwgu, pw, L.g_dx, px, dt, part, st, "tp_swiglu_bwd dWg/dWu GEMM",
+                         "tp_swiglu_bwd dX GEMM"))
+      return e;
   }
   return ok();
 }
@@ -664,35 +730,32 @@ int tp_attn_proj_fwd(int dt, int64_t s, int64_t h, int64_t dq, int64_t dkv, cons
       c.ptr(V, nk, "V") && c.ptr(Y, nx, "Y");
   if (c.status) return c.status;
   hipStream_t st = (hipStream_t)stream;
-  {  // [Q | K | V] = X . [Wq | Wk | Wv]: one launch, three N-segments
-    Spec g;
-    g.layout = GEMM_NN;
-    g.epi = EPI_STORE;
-    g.M = s;
-    g.K = h;
-    g.nseg = 3;
-    g.seg[0] = dq;
-    g.seg[1] = g.seg[2] = dkv;
-    g.N = dq + 2 * dkv;
-    g.ld(h);
-    g.ld(dq);
-    g.ld(dkv);
-    Ptrs p;
-    p.A[0] = X; p.lda[0] = h;
-    p.B[0] = Wq; p.B[1] = Wk; p.B[2] = Wv;
-    p.ldb[0] = dq; p.ldb[1] = p.ldb[2] = dkv;
-    p.C[0] = Q; p.C[1] = K; p.C[2] = V;
-    p.ldc[0] = dq; p.ldc[1] = p.ldc[2] = dkv;
-    if (int e = run(g, p, dt, nullptr, st, "tp_attn_proj_fwd QKV GEMM")) return e;
-  }
-  {  // Y = O . Wo
-    Spec g = spec_nn(s, h, dq, EPI_STORE);
-    Ptrs p;
-    p.A[0] = O; p.lda[0] = dq;
-    p.B[0] = Wo; p.ldb[0] = h;
-    p.C[0] = Y; p.ldc[0] = h;
-    if (int e = run(g, p, dt, nullptr, st, "tp_attn_proj_fwd output GEMM")) return e;
-  }
+  // [Q | K | V] = X . [Wq | Wk | Wv] (three N-segments)  beside  Y = O . Wo
+  Spec gq;
+  gq.layout = GEMM_NN;
+  gq.epi = EPI_STORE;
+  gq.M = s;
+  gq.K = h;
+  gq.nseg = 3;
+  gq.seg[0] = dq;
+  gq.seg[1] = gq.seg[2] = dkv;
+  gq.N = dq + 2 * dkv;
+  gq.ld(h);
+  gq.ld(dq);
+  gq.ld(dkv);
+  Ptrs pq;
+  pq.A[0] = X; pq.lda[0] = h;
+  pq.B[0] = Wq; pq.B[1] = Wk; pq.B[2] = Wv;
+  pq.ldb[0] = dq; pq.ldb[1] = pq.ldb[2] = dkv;
+  pq.C[0] = Q; pq.C[1] = K; pq.C[2] = V;
+  pq.ldc[0] = dq; pq.ldc[1] = pq.ldc[2] = dkv;
+  const Spec go = spec_nn(s, h, dq, EPI_STORE);
+  Ptrs po;
+  po.A[0] = O; po.lda[0] = dq;
+  po.B[0] = Wo; po.ldb[0] = h;
+  po.C[0] = Y; po.ldc[0] = h;
+  if (int e = run_pair(gq, pq, go, po, dt, nullptr, st, "tp_attn_proj_fwd QKV GEMM", "tp_attn_proj_fwd output GEMM"))
+    return e;
   return ok();
 }
 
@@ -723,37 +786,34 @@ int tp_attn_proj_bwd(int dt, int64_t s, int64_t h, int64_t dq, int64_t dkv, cons
   ws_ok(c, ws, ws_bytes, L.total, "tp_attn_proj_bwd");
   if (c.status) return c.status;
   hipStream_t st = (hipStream_t)stream;
-  {  // dX = dQ.Wq^T + dK.Wk^T + dV.Wv^T: one launch, three K-segments
-    Ptrs p;
-    p.A[0] = dQ; p.A[1] = dK; p.A[2] = dV;
-    p.lda[0] = dq; p.lda[1] = p.lda[2] = dkv;
-    p.B[0] = Wq; p.B[1] = Wk; p.B[2] = Wv;
-    p.ldb[0] = dq; p.ldb[1] = p.ldb[2] = dkv;
-    p.C[0] = dX; p.ldc[0] = h;
-    if (int e = run(L.g_dx, p, dt, ws, st, "tp_attn_proj_bwd dX GEMM")) return e;
+  {  // [dWq | dWk | dWv] = X^T . [dQ | dK | dV]  beside  dX = dQ.Wq^T + dK.Wk^T + dV.Wv^T (K-segments)
+    Ptrs pw;
+    pw.A[0] = X; pw.lda[0] = h;
+    pw.B[0] = dQ; pw.B[1] = dK; pw.B[2] = dV;
+    pw.ldb[0] = dq; pw.ldb[1] = pw.ldb[2] = dkv;
+    pw.C[0] = dWq; pw.C[1] = dWk; pw.C[2] = dWv;
+    pw.ldc[0] = dq; pw.ldc[1] = pw.ldc[2] = dkv;
+    Ptrs px;
+    px.A[0] = dQ; px.A[1] = dK; px.A[2] = dV;
+    px.lda[0] = dq; px.lda[1] = px.lda[2] = dkv;
+    px.B[0] = Wq; px.B[1] = Wk; px.B[2] = Wv;
+    px.ldb[0] = dq; px.ldb[1] = px.ldb[2] = dkv;
+    px.C[0] = dX; px.ldc[0] = h;
+    if (int e = run_pair(L.g_dwqkv, pw, L.g_dx, px, dt, ws, st, "tp_attn_proj_bwd dWqkv GEMM",
+                         "tp_attn_proj_bwd dX GEMM"))
+      return e;
   }
-  {  // [dWq | dWk | dWv] = X^T . [dQ | dK | dV]
-    Ptrs p;
-    p.A[0] = X; p.lda[0] = h;
-    p.B[0] = dQ; p.B[1] = dK; p.B[2] = dV;
-    p.ldb[0] = dq; p.ldb[1] = p.ldb[2] = dkv;
-    p.C[0] = dWq; p.C[1] = dWk; p.C[2] = dWv;
-    p.ldc[0] = dq; p.ldc[1] = p.ldc[2] = dkv;
-    if (int e = run(L.g_dwqkv, p, dt, ws, st, "tp_attn_proj_bwd dWqkv GEMM")) return e;
-  }
-  {  // dO = dY . Wo^T
-    Ptrs p;
-    p.A[0] = dY; p.lda[0] = h;
-    p.B[0] = Wo; p.ldb[0] = h;
-    p.C[0] = dO; p.ldc[0] = dq;
-    if (int e = run(L.g_do, p, dt, ws, st, "tp_attn_proj_bwd dO GEMM")) return e;
-  }
-  {  // dWo = O^T . dY
-    Ptrs p;
-    p.A[0] = O; p.lda[0] = dq;
-    p.B[0] = dY; p.ldb[0] = h;
-    p.C[0] = dWo; p.ldc[0] = h;
-    if (int e = run(L.g_dwo, p, dt, ws, st, "tp_attn_proj_bwd dWo GEMM")) return e;
+  {  // dWo = O^T . dY  beside  dO = dY . Wo^T
+    Ptrs pw;
+    pw.A[0] = O; pw.lda[0] = dq;
+    pw.B[0] = dY; pw.ldb[0] = h;
+    pw.C[0] = dWo; pw.ldc[0] = h;
+    Ptrs po;
+    po.A[0] = dY; po.lda[0] = h;
+    po.B[0] = Wo; po.ldb[0] = h;
+    po.C[0] = dO; po.ldc[0] = dq;
+    if (int e = run_pair(L.g_dwo, pw, L.g_do, po, dt, ws, st, "tp_attn_proj_bwd dWo GEMM", "tp_attn_proj_bwd dO GEMM"))
+      return e;
   }
   return ok();
 }
