@@ -248,14 +248,29 @@ __device__ __forceinline__ void epi8(const GemmDesc &d, int gm, int gn, int nlen
         }
       }
     }
+    // the activation kind is uniform: branch once per run of 8 so that the 8
+    // independent element chains interleave
+    if constexpr (EPI == EPI_ACT_FWD) {
+      if (d.act == ACT_GELU) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) y[q] = tp_gelu(x[q]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) y[q] = tp_relu(x[q]);
+      }
+    } else if constexpr (EPI == EPI_ACT_BWD) {
+      if (d.act == ACT_GELU) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) y[q] = x[q] * tp_gelu_grad(a0[q]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) y[q] = x[q] * tp_relu_grad(a0[q]);
+      }
+    }
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       if constexpr (EPI == EPI_STORE) {
         y[q] = x[q];
-      } else if constexpr (EPI == EPI_ACT_FWD) {
-        y[q] = tp_act_fwd(d.act, x[q]);
-      } else if constexpr (EPI == EPI_ACT_BWD) {
-        y[q] = x[q] * tp_act_grad(d.act, a0[q]);
       } else if constexpr (EPI == EPI_SWIGLU_FWD) {
         y[q] = x[q] * tp_sigmoid(x[q]) * u[q];
       } else if constexpr (EPI == EPI_SWIGLU_BWD) {

@@ -86,15 +86,20 @@ __device__ __forceinline__ float tp_gauss(float z) {  // exp(-z^2 / 2)
   return tp_exp2(-0.72134752044448170f * z * z);     // log2(e) / 2
 }
 
-__device__ __forceinline__ float tp_act_fwd(int act, float z) {
-  if (act == ACT_RELU) return z > 0.f ? z : 0.f;
-  return z * tp_phi_cdf(z, tp_gauss(z));  // GeLU, exact form z * Phi(z)
+__device__ __forceinline__ float tp_relu(float z) { return z > 0.f ? z : 0.f; }
+__device__ __forceinline__ float tp_relu_grad(float z) { return z > 0.f ? 1.f : 0.f; }
+__device__ __forceinline__ float tp_gelu(float z) {  // exact form z * Phi(z)
+  return z * tp_phi_cdf(z, tp_gauss(z));
 }
-
-__device__ __forceinline__ float tp_act_grad(int act, float z) {
-  if (act == ACT_RELU) return z > 0.f ? 1.f : 0.f;
+__device__ __forceinline__ float tp_gelu_grad(float z) {  // Phi(z) + z phi(z)
   const float e = tp_gauss(z);
-  return fmaf(z * 0.39894228040143268f, e, tp_phi_cdf(z, e));  // Phi(z) + z phi(z)
+  return fmaf(z * 0.39894228040143268f, e, tp_phi_cdf(z, e));
+}
+__device__ __forceinline__ float tp_act_fwd(int act, float z) {
+  return act == ACT_RELU ? tp_relu(z) : tp_gelu(z);
+}
+__device__ __forceinline__ float tp_act_grad(int act, float z) {
+  return act == ACT_RELU ? tp_relu_grad(z) : tp_gelu_grad(z);
 }
 
 __device__ __forceinline__ float tp_sigmoid(float z) {
