@@ -112,7 +112,7 @@ def build_rows(torch, which, only=None):
         return rows
     if want("swiglu_fwd", "swiglu_bwd", "attn_proj_fwd", "attn_proj_bwd"):
         rows += layer_rows(torch, up, bf, I, T, want)
-    if want("lm_head_fwd", "vocab_ce", "vocab_embed"):
+    if want("lm_head_fwd", "vocab_ce", "vocab_embed", "lm_head_ce_fused"):
         rows += vocab_rows(torch, up, bf, I, T)
     return rows
 
@@ -199,6 +199,13 @@ def vocab_rows(torch, up, bf, I, T):
                     bytes_=4.0 * s5 * Vs + 8.0 * s5 + 12.0 * s5))
     rows.append(Row("vocab_embed", c5, lambda: T.tp_vocab_embed(BF, s5, Vs, h5, 0, ids, table, emb),
                     bytes_=2.0 * s5 * h5 + 2.0 * n_in * h5 + 8.0 * s5))
+    # the fused form: LM head with the CE statistics in its epilogue, logits never stored
+    nbf = T.tp_lm_head_ce_workspace(BF, s5, h5, Vs)
+    wsf = torch.empty(max(nbf, 256), dtype=torch.uint8, device=dev)
+    fm, fse, ftl = (torch.empty(s5, dtype=torch.float32, device=dev) for _ in range(3))
+    rows.append(Row("lm_head_ce_fused", c5,
+                    lambda: T.tp_lm_head_ce_fwd(BF, s5, h5, Vs, 0, Hf, Wlm, tgt, fm, fse, ftl, wsf, nbf),
+                    flops=2.0 * s5 * h5 * Vs))
     return rows
 
 

@@ -188,6 +188,22 @@ int tp_vocab_ce(int64_t s, int64_t Vs, int64_t vocab_start,
                 const float *logits, const int64_t *target,
                 float *lmax, float *lsumexp, float *tlogit, void *stream);
 
+/* LM head and cross-entropy statistics in one pass, the logits never written
+ * ([lec16] §5.5: the fused vocab-parallel cross entropy keeps the [s, V/t]
+ * logit slice on chip and hands on three scalars per position).  Same outputs
+ * as tp_lm_head_fwd followed by tp_vocab_ce on its logits: lmax and tlogit
+ * are the same fp32 values, lsumexp the same sum in another order (within
+ * fp32 rounding).  Hf [s,h], Wlm [h,Vs], target [s] global ids; dt must be
+ * TP_DT_BF16 (TP_EUNSUPPORTED otherwise).  ws: device scratch of at least
+ * tp_lm_head_ce_workspace(dt, s, h, Vs) bytes, 256-byte aligned, overwritten
+ * (per-position partial statistics of every column block, about
+ * 12 * s * Vs / 128 bytes). */
+size_t tp_lm_head_ce_workspace(int dt, int64_t s, int64_t h, int64_t Vs);
+int tp_lm_head_ce_fwd(int dt, int64_t s, int64_t h, int64_t Vs, int64_t vocab_start,
+                      const void *Hf, const void *Wlm, const int64_t *target,
+                      float *lmax, float *lsumexp, float *tlogit,
+                      void *ws, size_t ws_bytes, void *stream);
+
 /* Embedding rows of a vocab shard: out[r,:] = table[ids[r]-vocab_start, :]
  * when vocab_start <= ids[r] < vocab_start+Vs, else the zero vector (all bits
  * 0).  table [Vs,h], out [n,h]; dt is the element type (rows are copied bit

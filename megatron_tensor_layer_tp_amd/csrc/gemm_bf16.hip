@@ -55,6 +55,7 @@ hipError_t tp_launch_gemm_bf16(const GemmDesc &d, int layout, int epi, bool out_
     case EPI_ACT_FWD: e = launch_shape<true, false, EPI_ACT_FWD, false>(d, bm, bn, st, vec); break;
     case EPI_SWIGLU_FWD: e = launch_shape<true, false, EPI_SWIGLU_FWD, false>(d, bm, bn, st, vec); break;
     case EPI_PARTIAL: e = launch_shape<true, false, EPI_PARTIAL, true>(d, bm, bn, st, vec); break;
+    case EPI_CE_STATS: e = launch_shape<true, false, EPI_CE_STATS, true>(d, bm, bn, st, vec); break;
     default: return hipErrorInvalidValue;
     }
     break;

@@ -303,6 +303,73 @@ __device__ __forceinline__ void epi8(const GemmDesc &d, int gm, int gn, int nlen
   }
 }
 
+// Reductions over the LPR (8 or 16) consecutive lanes of a DPP row with DPP
+// moves (VALU, no LDS round trip): xor 1 and xor 2 within quads, then the
+// half-row and row mirrors; every lane of the group ends with the result.
+template <int LPR>
+__device__ __forceinline__ float row_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true)));
+  if constexpr (LPR == 16)
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true)));
+  return v;
+}
+template <int LPR>
+__device__ __forceinline__ float row_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));
+  if constexpr (LPR == 16) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true));
+  return v;
+}
+
+// Cross-entropy statistics of the LM head's logits without storing them
+// (lecture 16 notes §5.5, the fused vocab-parallel cross entropy): the LPR
+// lanes holding row gm's columns of one wave's half-tile (8 each, from gn)
+// reduce them to the row's max over the valid columns and the sum of
+// exp(z - max); the lane holding the target id's column (if any) records its
+// logit.  Partials go to ws[gm][k][part] (k = max, sum, target logit; part =
+// this half-tile's index); the target slot is written only by the part that
+// holds the target.  Every lane must call it (cross-lane moves); rows >= M
+// write nothing.
+template <int LPR>
+__device__ __forceinline__ void ce_stats8(const GemmDesc &d, int gm, int gn, int nlen, int part, int lane,
+                                          const float *x) {
+  static_assert(LPR == 8 || LPR == 16, "row reductions span 8 or 16 lanes");
+  constexpr float LOG2E = 1.4426950408889634f;
+  const int nv = min(8, nlen - gn);  // valid columns of this lane (may be <= 0)
+  float mx = -INFINITY;
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    if (q < nv) mx = fmaxf(mx, x[q]);
+  mx = row_max<LPR>(mx);
+  float se = 0.f;
+  if (mx != -INFINITY) {
+    const float mb = mx * LOG2E;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (q < nv) se += tp_exp2(fmaf(x[q], LOG2E, -mb));
+  }
+  se = row_sum<LPR>(se);
+  if (gm < d.M) {
+    const int P = 2 * d.tiles_n;
+    float *w = d.ws + (int64_t)gm * 3 * P + part;
+    if (lane % LPR == 0) {
+      w[0] = mx;
+      w[P] = se;
+    }
+    const int64_t j = ((const int64_t *)d.ai0)[gm] - d.vstart - gn;
+    if (j >= 0 && j < nv) {
+      float t = x[0];
+#pragma unroll
+      for (int q = 1; q < 8; ++q)
+        if (j == q) t = x[q];
+      w[2 * P] = t;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Epilogue shared by both kernels.  Each wave stages one 32-row strip of its
 // accumulators at a time through LDS (fp32, rows padded by 8 floats so the
@@ -347,7 +414,11 @@ __device__ __forceinline__ void epilogue(const GemmDesc &d, f32x16 (&acc)[BM / 6
       }
       const int gm = m0 + wm * WTM + fm * 32 + r;
       const int gn = col_base + c;
-      if (gm < d.M && gn < nlen) epi8<EPI, OUT_F32, VEC>(d, gm, gn, nlen, sc, split, x, u);
+      if constexpr (EPI == EPI_CE_STATS) {
+        ce_stats8<LPR>(d, gm, gn, nlen, col_base / WTN, lane, x);
+      } else {
+        if (gm < d.M && gn < nlen) epi8<EPI, OUT_F32, VEC>(d, gm, gn, nlen, sc, split, x, u);
+      }
     }
   }
 }

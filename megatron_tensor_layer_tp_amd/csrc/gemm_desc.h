@@ -26,6 +26,8 @@ enum EpiKind : int {
   EPI_SWIGLU_FWD = 3,  // dual: ao0 = g, ao1 = u, C = SiLU(g) * u
   EPI_SWIGLU_BWD = 4,  // C = acc * ai1 * SiLU'(ai0) (dG); ao0 = acc * SiLU(ai0) (dU)
   EPI_PARTIAL = 5,     // fp32 split-K partial into ws[split][M][N]
+  EPI_CE_STATS = 6,    // logits stay on chip: per row and per half-tile of columns,
+                       // (max, sum exp(z - max), target logit) into ws[M][3][P]
 };
 
 enum ActKind : int { ACT_RELU = 0, ACT_GELU = 1 };
@@ -45,7 +47,8 @@ struct GemmDesc {
   int64_t ldb[TP_MAX_SEG];
   void *C[TP_MAX_SEG];
   int64_t ldc[TP_MAX_SEG];
-  const void *ai0, *ai1;           // epilogue inputs, indexed like C (one segment)
+  const void *ai0, *ai1;           // epilogue inputs, indexed like C (one segment);
+                                   // EPI_CE_STATS: ai0 = int64 target ids [M]
   int64_t ldai;
   void *ao0, *ao1;                 // epilogue extra outputs, indexed like C
   int64_t ldao;
@@ -54,6 +57,7 @@ struct GemmDesc {
   int32_t kt_per_split;            // K-tiles handled by one split
   int32_t tiles_m, tiles_n;        // tile grid (tiles_n counts all N-segments)
   int32_t group_m;                 // tile-rows per L2 group
+  int64_t vstart;                  // EPI_CE_STATS: global id of column 0
 };
 
 // ---------------------------------------------------------------------------

@@ -34,5 +34,8 @@ hipError_t tp_launch_gemm_f32(const GemmDesc &d, int layout, int epi, hipStream_
 
 hipError_t tp_launch_vocab_ce(int64_t s, int64_t Vs, int64_t start, const float *z, const int64_t *tgt,
                               float *m, float *se, float *tl, hipStream_t st);
+// merge the fused LM-head GEMM's per-part CE statistics ws [s][3][P] (parts of W columns)
+hipError_t tp_launch_ce_merge(const float *ws, int P, int W, int64_t s, int64_t Vs, int64_t start,
+                              const int64_t *tgt, float *m, float *se, float *tl, hipStream_t st);
 hipError_t tp_launch_vocab_embed(int elem_bytes, int64_t n, int64_t Vs, int64_t h, int64_t start,
                                  const int64_t *ids, const void *table, void *out, hipStream_t st);

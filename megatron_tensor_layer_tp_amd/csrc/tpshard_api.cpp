@@ -499,6 +499,24 @@ AttnBwdLayout attn_bwd_layout(int dt, int64_t s, int64_t h, int64_t dq, int64_t 
   return L;
 }
 
+// fused LM head + CE statistics: the GEMM's plan and its partial-statistics workspace
+struct LmCePlan {
+  Spec g;
+  Plan p;
+  int parts = 0, width = 0;
+  size_t bytes = 0;
+};
+LmCePlan lm_ce_plan(int64_t s, int64_t h, int64_t Vs) {
+  LmCePlan L;
+  L.g = spec_nn(s, Vs, h, EPI_CE_STATS);
+  L.g.out_f32 = true;
+  L.p = plan_bf16(L.g);
+  L.parts = 2 * L.p.tiles_n;
+  L.width = L.p.bn / 2;
+  L.bytes = align256((size_t)s * 3 * L.parts * sizeof(float));
+  return L;
+}
+
 bool ws_ok(Checker &c, const void *ws, size_t have, size_t need, const char *call) {
   if (c.status) return false;
   if (need == 0) return true;
@@ -851,6 +869,44 @@ int tp_vocab_ce(int64_t s, int64_t Vs, int64_t vocab_start, const float *logits,
   hipError_t e = tp_launch_vocab_ce(s, Vs, vocab_start, logits, target, lmax, lsumexp, tlogit,
                                     (hipStream_t)stream);
   if (e != hipSuccess) return fail(TP_EHIP, "tp_vocab_ce: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t tp_lm_head_ce_workspace(int dt, int64_t s, int64_t h, int64_t Vs) {
+  Checker c;
+  c.dtype(dt, false, "tp_lm_head_ce_workspace");
+  c.dim(s, "s") && c.dim(h, "h") && c.dim(Vs, "Vs");
+  if (c.status) return 0;
+  return lm_ce_plan(s, h, Vs).bytes;
+}
+
+int tp_lm_head_ce_fwd(int dt, int64_t s, int64_t h, int64_t Vs, int64_t vocab_start, const void *Hf,
+                      const void *Wlm, const int64_t *target, float *lmax, float *lsumexp, float *tlogit,
+                      void *ws, size_t ws_bytes, void *stream) {
+  Checker c;
+  int64_t nh, nw;
+  c.dtype(dt, false, "tp_lm_head_ce_fwd");
+  c.dim(s, "s") && c.dim(h, "h") && c.dim(Vs, "Vs");
+  if (!c.status && vocab_start < 0) c.status = fail(TP_ESHAPE, "vocab_start = %lld < 0", (long long)vocab_start);
+  c.elems(s, h, nh, "Hf") && c.elems(h, Vs, nw, "Wlm");
+  c.ptr(Hf, nh, "Hf") && c.ptr(Wlm, nw, "Wlm") && c.ptr(target, s, "target") && c.ptr(lmax, s, "lmax") &&
+      c.ptr(lsumexp, s, "lsumexp") && c.ptr(tlogit, s, "tlogit");
+  if (c.status) return c.status;
+  const LmCePlan L = lm_ce_plan(s, h, Vs);
+  ws_ok(c, ws, ws_bytes, L.bytes, "tp_lm_head_ce_fwd");
+  if (c.status) return c.status;
+  hipStream_t st = (hipStream_t)stream;
+  Ptrs q;
+  q.A[0] = Hf; q.lda[0] = h;
+  q.B[0] = Wlm; q.ldb[0] = Vs;
+  q.ai0 = target;
+  GemmDesc d = make_desc(L.g, q, L.p, TP_DT_BF16, ws);
+  d.vstart = vocab_start;
+  hipError_t e = tp_launch_gemm_bf16(d, GEMM_NN, EPI_CE_STATS, true, L.p.bm, L.p.bn, L.p.vec, st);
+  if (e == hipSuccess)
+    e = tp_launch_ce_merge((const float *)ws, L.parts, L.width, s, Vs, vocab_start, target, lmax, lsumexp, tlogit,
+                           st);
+  if (e != hipSuccess) return fail(TP_EHIP, "tp_lm_head_ce_fwd: %s", hipGetErrorString(e));
   return ok();
 }
 

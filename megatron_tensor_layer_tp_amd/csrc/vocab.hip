@@ -94,6 +94,40 @@ __global__ void __launch_bounds__(CE_THREADS) vocab_ce_kernel(const float *__res
   }
 }
 
+// Merge the per-half-tile statistics of the fused LM-head GEMM into the
+// shard's three numbers per position: one wave per row reads its P partials
+// ws[row][k][p] (k = max, sum exp, target logit), takes M = max_p m_p and
+// S = sum_p se_p exp(m_p - M) in a fixed order, and picks the target's logit
+// from the part of width W that holds column target - start.
+__global__ void __launch_bounds__(256) ce_merge_kernel(const float *__restrict__ ws, int P, int W, int64_t s,
+                                                       int64_t Vs, int64_t start,
+                                                       const int64_t *__restrict__ tgt,
+                                                       float *__restrict__ m_out, float *__restrict__ se_out,
+                                                       float *__restrict__ tl_out) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= s) return;
+  const float *w = ws + row * 3 * (int64_t)P;
+  float mx = -INFINITY;
+  for (int p = lane; p < P; p += 64) mx = fmaxf(mx, w[p]);
+  mx = wave_max(mx);
+  float sum = 0.f;
+  if (mx != -INFINITY) {
+    const float mb = mx * LOG2E;
+    for (int p = lane; p < P; p += 64) {
+      const float mp = w[p];
+      if (mp != -INFINITY) sum += w[P + p] * exp2f(fmaf(mp, LOG2E, -mb));
+    }
+  }
+  sum = wave_sum(sum);
+  if (lane == 0) {
+    const int64_t y = tgt[row];
+    m_out[row] = mx;
+    se_out[row] = sum;
+    tl_out[row] = (y >= start && y - start < Vs) ? w[2 * P + (y - start) / W] : 0.f;
+  }
+}
+
 // One workgroup per output row: copy the owned table row, or write zeros.
 template <typename T>
 __global__ void __launch_bounds__(256) vocab_embed_kernel(int64_t n, int64_t Vs, int64_t nelem,
@@ -127,6 +161,14 @@ hipError_t tp_launch_vocab_ce(int64_t s, int64_t Vs, int64_t start, const float 
     hipLaunchKernelGGL(vocab_ce_kernel<4>, dim3(grid), dim3(CE_THREADS), 0, st, z, tgt, s, Vs, start, m, se, tl);
   else
     hipLaunchKernelGGL(vocab_ce_kernel<1>, dim3(grid), dim3(CE_THREADS), 0, st, z, tgt, s, Vs, start, m, se, tl);
+  return hipGetLastError();
+}
+
+hipError_t tp_launch_ce_merge(const float *ws, int P, int W, int64_t s, int64_t Vs, int64_t start,
+                              const int64_t *tgt, float *m, float *se, float *tl, hipStream_t st) {
+  if (s == 0) return hipSuccess;
+  hipLaunchKernelGGL(ce_merge_kernel, dim3((unsigned)((s + 3) / 4)), dim3(256), 0, st, ws, P, W, s, Vs, start,
+                     tgt, m, se, tl);
   return hipGetLastError();
 }
 

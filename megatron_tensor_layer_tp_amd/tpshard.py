@@ -36,6 +36,8 @@ _SIGS = {
     "tp_attn_proj_bwd": (_int, [_int, _i64, _i64, _i64, _i64] + [_vp] * 16 + [_vp, _sz, _vp]),
     "tp_lm_head_fwd": (_int, [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
     "tp_vocab_ce": (_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "tp_lm_head_ce_workspace": (_sz, [_int, _i64, _i64, _i64]),
+    "tp_lm_head_ce_fwd": (_int, [_int, _i64, _i64, _i64, _i64] + [_vp] * 6 + [_vp, _sz, _vp]),
     "tp_vocab_embed": (_int, [_int, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
     "tp_status_string": (ctypes.c_char_p, [_int]),
     "tp_last_error": (ctypes.c_char_p, []),
@@ -160,6 +162,16 @@ def tp_attn_proj_bwd(dt, s, h, dq, dkv, X, Wq, Wk, Wv, O, Wo, dQ, dK, dV, dY, dX
 # ---------------------------------------------------------------- vocab
 def tp_lm_head_fwd(dt, s, h, Vs, Hf, Wlm, logits, stream=None):
     return _call("tp_lm_head_fwd", dt, s, h, Vs, _ptr(Hf), _ptr(Wlm), _ptr(logits), _stream(stream))
+
+
+def tp_lm_head_ce_workspace(dt, s, h, Vs):
+    return lib().tp_lm_head_ce_workspace(dt, s, h, Vs)
+
+
+def tp_lm_head_ce_fwd(dt, s, h, Vs, vocab_start, Hf, Wlm, target, lmax, lsumexp, tlogit, ws, ws_bytes,
+                      stream=None):
+    return _call("tp_lm_head_ce_fwd", dt, s, h, Vs, vocab_start, _ptr(Hf), _ptr(Wlm), _ptr(target), _ptr(lmax),
+                 _ptr(lsumexp), _ptr(tlogit), _ptr(ws), ws_bytes, _stream(stream))
 
 
 def tp_vocab_ce(s, Vs, vocab_start, logits, target, lmax, lsumexp, tlogit, stream=None):

@@ -34,7 +34,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert len(names) == 15, names
+    assert len(names) == 17, names
     raw = ctypes.CDLL(T.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -119,3 +119,26 @@ def test_layer_calls_validation(L):
     # zero-width K/V heads are legal sizes (nothing to write for them)
     ok = [T.TP_DT_BF16, 0, 16, 16, 0] + [A16, A16, None, None, None, A16, A16, None, None, None] + [None]
     assert _st(L, "tp_attn_proj_fwd", *ok) == T.TP_OK
+
+
+def test_lm_head_ce_validation(L):
+    need = T.tp_lm_head_ce_workspace(T.TP_DT_BF16, 8192, 8192, 16032)
+    # three fp32 partials per position for every half-tile of columns
+    assert need >= 8192 * 3 * 4 * (2 * (16032 // 256))
+    assert need == T.tp_lm_head_ce_workspace(T.TP_DT_BF16, 8192, 8192, 16032)
+    assert T.tp_lm_head_ce_workspace(T.TP_DT_F32, 8, 8, 8) == 0
+    args = [T.TP_DT_BF16, 8192, 8192, 16032, 0] + [A16] * 6
+    bad = list(args)
+    bad[0] = T.TP_DT_F32
+    assert _st(L, "tp_lm_head_ce_fwd", *bad, A16, need, None) == T.TP_EUNSUPPORTED
+    bad = list(args)
+    bad[4] = -1
+    assert _st(L, "tp_lm_head_ce_fwd", *bad, A16, need, None) == T.TP_ESHAPE
+    bad = list(args)
+    bad[7] = None  # target
+    assert _st(L, "tp_lm_head_ce_fwd", *bad, A16, need, None) == T.TP_EINVAL
+    assert _st(L, "tp_lm_head_ce_fwd", *args, A16, need - 1, None) == T.TP_EWORKSPACE
+    assert _st(L, "tp_lm_head_ce_fwd", *args, A16 + 16, need, None) == T.TP_EALIGN
+    # nothing to compute: no positions
+    assert _st(L, "tp_lm_head_ce_fwd", T.TP_DT_BF16, 0, 64, 100, 0, None, A16, None, None, None, None,
+               None, 0, None) == T.TP_OK
