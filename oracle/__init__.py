@@ -58,6 +58,7 @@ def _L():
         lib.or_ce_stats.argtypes = [_i64, _i64, _i64, _d, ctypes.c_void_p, _d, _d, _d]
         lib.or_ce_combine.argtypes = [_i64, _i64, _d, _d, _d, _d]
         lib.or_ce_direct.argtypes = [_i64, _i64, _d, ctypes.c_void_p, _d]
+        lib.or_ce_bwd.argtypes = [_i64, _i64, _i64, _d, ctypes.c_void_p, _d, _d, _d, _d]
         lib.or_embed_u16.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_void_p,
                                      ctypes.c_void_p, ctypes.c_void_p]
         lib.or_embed_u32.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_void_p,
@@ -315,6 +316,29 @@ def ce_combine(ms, ses, tls):
     if s:
         _L().or_ce_combine(t, s, _p(m), _p(se), _p(tl), _p(loss))
     return loss
+
+
+def ce_global(ms, ses):
+    """The combined (M, S) per position from the shards' (m_i, se_i):
+    M = max_i m_i, S = sum_i se_i exp(m_i - M) (shards with no columns add 0)."""
+    m = _f64(np.stack(ms))
+    se = _f64(np.stack(ses))
+    M = m.max(axis=0)
+    w = np.where(se > 0, se * np.exp(np.where(se > 0, m - M, 0.0)), 0.0)
+    return M, w.sum(axis=0)
+
+
+def ce_bwd(logits, targets, vocab_start: int, M, S, g):
+    """dz = g * (exp(z - M) / S - onehot(target)) on one shard's [s, Vs] slice,
+    with M, S the combined statistics and g the incoming gradient per position."""
+    z = _f64(logits)
+    s, Vs = z.shape
+    tg = np.ascontiguousarray(targets, dtype=np.int64)
+    M, S, g = (_f64(np.asarray(a)) for a in (M, S, g))
+    dz = np.empty((s, Vs))
+    if s and Vs:
+        _L().or_ce_bwd(s, Vs, int(vocab_start), _p(z), tg.ctypes.data, _p(M), _p(S), _p(g), _p(dz))
+    return dz
 
 
 def ce_direct(logits_full, targets):

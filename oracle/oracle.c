@@ -148,6 +148,25 @@ void or_ce_combine(int64_t t, int64_t s, const double *m, const double *se,
     }
 }
 
+/* Gradient of the loss with respect to the shard's logits: the derivative of
+ * loss_r = logsumexp_j z[r,j] - z[r,y_r] is softmax minus the one-hot target,
+ *   dz[r,j] = g_r * (exp(z[r,j] - M_r) / S_r - [start + j == y_r]),
+ * where M_r and S_r are the combined maximum and sum of exponentials over the
+ * whole vocabulary (what the combine above reduces across shards) and g_r is
+ * the gradient arriving at loss_r. */
+void or_ce_bwd(int64_t s, int64_t Vs, int64_t start, const double *z, const int64_t *target,
+               const double *M, const double *S, const double *g, double *dz)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < s; ++r) {
+        for (int64_t j = 0; j < Vs; ++j) {
+            double p = exp(z[r * Vs + j] - M[r]) / S[r];
+            double onehot = (start + j == target[r]) ? 1.0 : 0.0;
+            dz[r * Vs + j] = g[r] * (p - onehot);
+        }
+    }
+}
+
 /* The unsharded definition: loss_r = logsumexp_j z[r,j] - z[r, y_r] over the
  * whole vocabulary [s, V]. */
 void or_ce_direct(int64_t s, int64_t V, const double *z, const int64_t *target,

@@ -133,3 +133,75 @@ def test_embedding_out_of_range_ids_give_zero_rows(oracle_mod):
     f32 = np.arange(6, dtype=np.float32).reshape(2, 3) + 1
     out32 = oracle_mod.embed(np.array([1, 2]), f32, 0)
     assert np.array_equal(out32, np.array([f32[1], [0, 0, 0]], dtype=np.float32))
+
+
+# ---------------------------------------------------------------- CE backward
+def _shard_grads(oracle_mod, z, y, t, g):
+    """Each shard's gradient slice from the combined (M, S), concatenated."""
+    V = z.shape[1]
+    Vs = V // t
+    ms, ses, _ = _split_stats(oracle_mod, z, y, t)
+    M, S = oracle_mod.ce_global(ms, ses)
+    parts = [oracle_mod.ce_bwd(np.ascontiguousarray(z[:, i * Vs:(i + 1) * Vs]), y, i * Vs, M, S, g)
+             for i in range(t)]
+    return np.concatenate(parts, axis=1)
+
+
+@pytest.mark.parametrize("t", [1, 2, 4, 8])
+def test_ce_bwd_matches_torch_autograd(oracle_mod, t):
+    """Sharded gradients, concatenated, equal torch's fp64 autograd of
+    cross_entropy with per-position upstream gradients."""
+    rng = np.random.default_rng(30 + t)
+    s, V = 12, 64
+    z = rng.standard_normal((s, V)) * 3
+    y = rng.integers(0, V, s)
+    g = rng.standard_normal(s)
+    zt = torch.tensor(z, requires_grad=True)
+    loss = torch.nn.functional.cross_entropy(zt, torch.tensor(y), reduction="none")
+    loss.backward(torch.tensor(g))
+    got = _shard_grads(oracle_mod, z, y, t, g)
+    np.testing.assert_allclose(got, zt.grad.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_ce_bwd_finite_differences(oracle_mod):
+    """Central differences of the direct loss, entry by entry, on a tiny case."""
+    rng = np.random.default_rng(7)
+    s, V, t = 3, 12, 3
+    z = rng.standard_normal((s, V)) * 2
+    y = np.array([0, 7, 11])
+    g = np.ones(s)
+    got = _shard_grads(oracle_mod, z, y, t, g)
+    eps = 1e-6
+    for r in range(s):
+        for j in range(V):
+            zp, zm = z.copy(), z.copy()
+            zp[r, j] += eps
+            zm[r, j] -= eps
+            fd = (oracle_mod.ce_direct(zp, y)[r] - oracle_mod.ce_direct(zm, y)[r]) / (2 * eps)
+            assert abs(got[r, j] - fd) <= 1e-8, (r, j, got[r, j], fd)
+
+
+def test_ce_bwd_invariants(oracle_mod):
+    """Every full row sums to 0 (softmax sums to 1, minus the one-hot); the
+    entries are p - 1 at the target and p >= 0 elsewhere; a target outside the
+    shard adds nothing to it; uniform logits give 1/V - onehot."""
+    rng = np.random.default_rng(8)
+    s, V, t = 6, 40, 4
+    z = rng.standard_normal((s, V)) * 5
+    y = rng.integers(0, V, s)
+    g = np.full(s, 0.5)
+    dz = _shard_grads(oracle_mod, z, y, t, g)
+    np.testing.assert_allclose(dz.sum(axis=1), 0.0, atol=1e-15)
+    mask = np.zeros_like(dz, dtype=bool)
+    mask[np.arange(s), y] = True
+    assert np.all(dz[~mask] >= 0) and np.all(dz[mask] < 0)
+    zu = np.full((2, V), -1.25)
+    yu = np.array([3, 39])
+    du = _shard_grads(oracle_mod, zu, yu, t, np.ones(2))
+    want = np.full((2, V), 1.0 / V)
+    want[[0, 1], yu] -= 1.0
+    np.testing.assert_allclose(du, want, rtol=1e-14, atol=1e-16)
+    # a shard that holds no target: its slice is the softmax slice only
+    M, S = oracle_mod.ce_global(*_split_stats(oracle_mod, z, y, 1)[:2])
+    sl = oracle_mod.ce_bwd(z[:, :10], np.full(s, 10_000), 0, M, S, np.ones(s))
+    np.testing.assert_allclose(sl, np.exp(z[:, :10] - M[:, None]) / S[:, None], rtol=1e-14)
