@@ -112,7 +112,7 @@ def build_rows(torch, which, only=None):
         return rows
     if want("swiglu_fwd", "swiglu_bwd", "attn_proj_fwd", "attn_proj_bwd"):
         rows += layer_rows(torch, up, bf, I, T, want)
-    if want("lm_head_fwd", "vocab_ce", "vocab_embed", "lm_head_ce_fused"):
+    if want("lm_head_fwd", "vocab_ce", "vocab_embed", "vocab_ce_bwd", "lm_head_ce_fused"):
         rows += vocab_rows(torch, up, bf, I, T)
     return rows
 
@@ -199,6 +199,12 @@ def vocab_rows(torch, up, bf, I, T):
                     bytes_=4.0 * s5 * Vs + 8.0 * s5 + 12.0 * s5))
     rows.append(Row("vocab_embed", c5, lambda: T.tp_vocab_embed(BF, s5, Vs, h5, 0, ids, table, emb),
                     bytes_=2.0 * s5 * h5 + 2.0 * n_in * h5 + 8.0 * s5))
+    # CE backward on the shard's logits: (M, S) of this shard stand in for the
+    # combined statistics; the gradient is stored bf16 for the LM head's backward
+    dlg = bf((s5, Vs))
+    gl = torch.full((s5,), 1.0 / s5, dtype=torch.float32, device=dev)
+    rows.append(Row("vocab_ce_bwd", c5, lambda: T.tp_vocab_ce_bwd(BF, s5, Vs, 0, logits, tgt, m, se, gl, dlg),
+                    bytes_=4.0 * s5 * Vs + 2.0 * s5 * Vs + 8.0 * s5 + 12.0 * s5))
     # the fused form: LM head with the CE statistics in its epilogue, logits never stored
     nbf = T.tp_lm_head_ce_workspace(BF, s5, h5, Vs)
     wsf = torch.empty(max(nbf, 256), dtype=torch.uint8, device=dev)
@@ -290,14 +296,16 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": 1 << 30, "launches": 3}))
         return
-    rows = build_rows(torch, args.rows, args.only if args.only != "vocab_ce" else "lm_head_fwd")
+    rows = build_rows(torch, args.rows, args.only if args.only not in ("vocab_ce", "vocab_ce_bwd") else "lm_head_fwd")
     if args.only:
         keep = [r for r in rows if r.name == args.only]
         if not keep:
             print(f"no row named {args.only}; rows: {[r.name for r in rows]}", file=sys.stderr)
             sys.exit(2)
-        if args.only == "vocab_ce":  # its input is the LM head's output: compute it once
+        if args.only in ("vocab_ce", "vocab_ce_bwd"):  # input: the LM head's output, computed once
             next(r for r in rows if r.name == "lm_head_fwd").fn()
+            if args.only == "vocab_ce_bwd":
+                next(r for r in rows if r.name == "vocab_ce").fn()
         rows = keep
     torch.cuda.synchronize()
     for _ in range(args.warmup):

@@ -188,6 +188,21 @@ int tp_vocab_ce(int64_t s, int64_t Vs, int64_t vocab_start,
                 const float *logits, const int64_t *target,
                 float *lmax, float *lsumexp, float *tlogit, void *stream);
 
+/* Backward of the vocab-parallel cross entropy on the shard's logit slice
+ * ([lec16] §5.5): with M[r], S[r] the combined maximum and sum of exponentials
+ * over the whole vocabulary (M = max_i lmax_i, S = sum_i lsumexp_i
+ * exp(lmax_i - M) over the shards) and dloss[r] the gradient arriving at
+ * position r's loss (1/s for a mean),
+ *     dlogits[r,j] = dloss[r] * (exp(z[r,j] - M[r]) / S[r] - [vocab_start + j == target[r]]),
+ * softmax minus the one-hot target, restricted to the shard's columns.
+ * logits [s,Vs] fp32; gmax, gsum, dloss [s] fp32 (gsum > 0, as any combine of
+ * a non-empty vocabulary gives); dlogits [s,Vs] fp32 (dt = TP_DT_F32) or bf16
+ * (dt = TP_DT_BF16).  A target outside the shard contributes no one-hot. */
+int tp_vocab_ce_bwd(int dt, int64_t s, int64_t Vs, int64_t vocab_start,
+                    const float *logits, const int64_t *target,
+                    const float *gmax, const float *gsum, const float *dloss,
+                    void *dlogits, void *stream);
+
 /* LM head and cross-entropy statistics in one pass, the logits never written
  * ([lec16] §5.5: the fused vocab-parallel cross entropy keeps the [s, V/t]
  * logit slice on chip and hands on three scalars per position).  Same outputs

@@ -34,6 +34,9 @@ hipError_t tp_launch_gemm_f32(const GemmDesc &d, int layout, int epi, hipStream_
 
 hipError_t tp_launch_vocab_ce(int64_t s, int64_t Vs, int64_t start, const float *z, const int64_t *tgt,
                               float *m, float *se, float *tl, hipStream_t st);
+hipError_t tp_launch_vocab_ce_bwd(bool bf16_out, int64_t s, int64_t Vs, int64_t start, const float *z,
+                                  const int64_t *tgt, const float *M, const float *S, const float *g, void *out,
+                                  hipStream_t st);
 // merge the fused LM-head GEMM's per-part CE statistics ws [s][3][P] (parts of W columns)
 hipError_t tp_launch_ce_merge(const float *ws, int P, int W, int64_t s, int64_t Vs, int64_t start,
                               const int64_t *tgt, float *m, float *se, float *tl, hipStream_t st);

@@ -872,6 +872,24 @@ int tp_vocab_ce(int64_t s, int64_t Vs, int64_t vocab_start, const float *logits,
   return ok();
 }
 
+int tp_vocab_ce_bwd(int dt, int64_t s, int64_t Vs, int64_t vocab_start, const float *logits,
+                    const int64_t *target, const float *gmax, const float *gsum, const float *dloss,
+                    void *dlogits, void *stream) {
+  Checker c;
+  int64_t nl;
+  c.dtype(dt, true, "tp_vocab_ce_bwd");
+  c.dim(s, "s") && c.dim(Vs, "Vs");
+  if (!c.status && vocab_start < 0) c.status = fail(TP_ESHAPE, "vocab_start = %lld < 0", (long long)vocab_start);
+  c.elems(s, Vs, nl, "logits");
+  c.ptr(logits, nl, "logits") && c.ptr(target, s, "target") && c.ptr(gmax, s, "gmax") &&
+      c.ptr(gsum, s, "gsum") && c.ptr(dloss, s, "dloss") && c.ptr(dlogits, nl, "dlogits");
+  if (c.status) return c.status;
+  hipError_t e = tp_launch_vocab_ce_bwd(dt == TP_DT_BF16, s, Vs, vocab_start, logits, target, gmax, gsum, dloss,
+                                        dlogits, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TP_EHIP, "tp_vocab_ce_bwd: %s", hipGetErrorString(e));
+  return ok();
+}
+
 size_t tp_lm_head_ce_workspace(int dt, int64_t s, int64_t h, int64_t Vs) {
   Checker c;
   c.dtype(dt, false, "tp_lm_head_ce_workspace");

@@ -94,6 +94,60 @@ __global__ void __launch_bounds__(CE_THREADS) vocab_ce_kernel(const float *__res
   }
 }
 
+// Gradient of the cross entropy with respect to one shard's logit slice
+// (lecture 16 notes §5.5: each shard differentiates its own slice once the
+// combined max M and sum S are known):
+//     dz[r,j] = g[r] * (exp(z[r,j] - M[r]) / S[r] - [start + j == target[r]]).
+// One workgroup per row streams the row once: 16-byte loads and stores (VW =
+// 4), fp32 or bf16 output.
+template <int VW, bool BF16_OUT>
+__global__ void __launch_bounds__(CE_THREADS) vocab_ce_bwd_kernel(const float *__restrict__ z,
+                                                                  const int64_t *__restrict__ tgt,
+                                                                  const float *__restrict__ Mg,
+                                                                  const float *__restrict__ Sg,
+                                                                  const float *__restrict__ g, int64_t s,
+                                                                  int64_t Vs, int64_t start,
+                                                                  void *__restrict__ out) {
+  typedef float vec_t __attribute__((ext_vector_type(VW)));
+  const int64_t nvec = Vs / VW;
+  for (int64_t row = blockIdx.x; row < s; row += gridDim.x) {
+    const float mb = Mg[row] * LOG2E;
+    const float gr = g[row];
+    const float scale = gr / Sg[row];
+    const int64_t y = tgt[row] - start;  // target column; outside [0, Vs) when not in the shard
+    const vec_t *p = (const vec_t *)(z + row * Vs);
+#pragma unroll 4
+    for (int64_t i = threadIdx.x; i < nvec; i += CE_THREADS) {
+      const vec_t v = p[i];
+      float o[VW];
+#pragma unroll
+      for (int e = 0; e < VW; ++e) {
+        o[e] = exp2f(fmaf(v[e], LOG2E, -mb)) * scale;
+        if (i * VW + e == y) o[e] -= gr;
+      }
+      if constexpr (BF16_OUT) {
+        uint16_t *dst = (uint16_t *)out + row * Vs + i * VW;
+        if constexpr (VW == 4) {
+          typedef float f2 __attribute__((ext_vector_type(2)));
+          typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+          const f2 lo = {o[0], o[1]}, hi = {o[2], o[3]};
+          uint2 w;
+          w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, b2));
+          w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, b2));
+          *(uint2 *)dst = w;
+        } else {
+          dst[0] = __builtin_bit_cast(uint16_t, (__bf16)o[0]);
+        }
+      } else {
+        vec_t w;
+#pragma unroll
+        for (int e = 0; e < VW; ++e) w[e] = o[e];
+        *((vec_t *)((float *)out + row * Vs) + i) = w;
+      }
+    }
+  }
+}
+
 // Merge the per-half-tile statistics of the fused LM-head GEMM into the
 // shard's three numbers per position: one wave per row reads its P partials
 // ws[row][k][p] (k = max, sum exp, target logit), takes M = max_p m_p and
@@ -169,6 +223,24 @@ hipError_t tp_launch_ce_merge(const float *ws, int P, int W, int64_t s, int64_t 
   if (s == 0) return hipSuccess;
   hipLaunchKernelGGL(ce_merge_kernel, dim3((unsigned)((s + 3) / 4)), dim3(256), 0, st, ws, P, W, s, Vs, start,
                      tgt, m, se, tl);
+  return hipGetLastError();
+}
+
+hipError_t tp_launch_vocab_ce_bwd(bool bf16_out, int64_t s, int64_t Vs, int64_t start, const float *z,
+                                  const int64_t *tgt, const float *M, const float *S, const float *g, void *out,
+                                  hipStream_t st) {
+  if (s == 0 || Vs == 0) return hipSuccess;
+  const unsigned grid = (unsigned)(s < 1048576 ? s : 1048576);
+  const bool v4 = Vs % 4 == 0 && (((uintptr_t)z | (uintptr_t)out) & 15) == 0;
+  const dim3 b(CE_THREADS);
+  if (v4 && bf16_out)
+    hipLaunchKernelGGL((vocab_ce_bwd_kernel<4, true>), dim3(grid), b, 0, st, z, tgt, M, S, g, s, Vs, start, out);
+  else if (v4)
+    hipLaunchKernelGGL((vocab_ce_bwd_kernel<4, false>), dim3(grid), b, 0, st, z, tgt, M, S, g, s, Vs, start, out);
+  else if (bf16_out)
+    hipLaunchKernelGGL((vocab_ce_bwd_kernel<1, true>), dim3(grid), b, 0, st, z, tgt, M, S, g, s, Vs, start, out);
+  else
+    hipLaunchKernelGGL((vocab_ce_bwd_kernel<1, false>), dim3(grid), b, 0, st, z, tgt, M, S, g, s, Vs, start, out);
   return hipGetLastError();
 }
 

@@ -34,7 +34,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     raw = ctypes.CDLL(T.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -142,3 +142,22 @@ def test_lm_head_ce_validation(L):
     # nothing to compute: no positions
     assert _st(L, "tp_lm_head_ce_fwd", T.TP_DT_BF16, 0, 64, 100, 0, None, A16, None, None, None, None,
                None, 0, None) == T.TP_OK
+
+
+def test_vocab_ce_bwd_validation(L):
+    args = [T.TP_DT_F32, 16, 32, 0] + [A16] * 6 + [None]
+    bad = list(args)
+    bad[0] = 3
+    assert _st(L, "tp_vocab_ce_bwd", *bad) == T.TP_EINVAL
+    bad = list(args)
+    bad[3] = -1
+    assert _st(L, "tp_vocab_ce_bwd", *bad) == T.TP_ESHAPE
+    bad = list(args)
+    bad[8] = None  # dloss
+    assert _st(L, "tp_vocab_ce_bwd", *bad) == T.TP_EINVAL
+    assert "dloss" in T.tp_last_error()
+    bad = list(args)
+    bad[9] = A16 + 4
+    assert _st(L, "tp_vocab_ce_bwd", *bad) == T.TP_EALIGN
+    # nothing to compute: an empty shard
+    assert _st(L, "tp_vocab_ce_bwd", T.TP_DT_BF16, 16, 0, 0, None, A16, A16, A16, A16, None, None) == T.TP_OK

@@ -6,6 +6,9 @@ lecture 16 notes §5.5) against the fp64 oracle.
   * CE statistics on seeded fp32 logit slices: max and target logit bit-exact,
     sum of exponentials <= 1e-5 relative, and the loss combined over all 8
     shards within 1e-4 absolute of the direct logsumexp - z[target].
+  * CE backward (softmax minus one-hot on the shard's slice): fp32 gradients
+    within 1e-5 relative Frobenius and 1e-6 absolute (scaled by the incoming
+    gradient), bf16 gradients within one bf16 rounding; full rows sum to 0.
   * Embedding: bit-exact rows, zero rows for ids outside the shard.
 """
 import numpy as np
@@ -117,6 +120,74 @@ def test_ce_loss_combined_over_shards(oracle_mod):
     direct = oracle_mod.ce_direct(z.astype(np.float64), tgt)
     assert np.abs(loss - direct).max() <= 1e-4
     assert abs(loss.mean() - direct.mean()) <= 1e-4
+
+
+# ---------------------------------------------------------------- CE backward
+def run_ce_bwd(z, tgt, start, M, S, g, bf16):
+    s, Vs = z.shape
+    out = fill_garbage(torch.empty((s, Vs), dtype=torch.int16 if bf16 else torch.float32, device="cuda:0"))
+    f32 = lambda a: dev(np.ascontiguousarray(a, np.float32))  # noqa: E731
+    T.tp_vocab_ce_bwd(T.TP_DT_BF16 if bf16 else T.TP_DT_F32, s, Vs, start, f32(z),
+                      dev(np.ascontiguousarray(tgt, np.int64)), f32(M), f32(S), f32(g), out)
+    torch.cuda.synchronize()
+    return host_f64(out)
+
+
+def check_ce_bwd(got, want, g, bf16):
+    if bf16:
+        assert rel_fro(got, want) <= 5e-3
+        # one bf16 rounding of the fp32 value
+        assert np.all(np.abs(got - want) <= 2.0 ** -8 * np.abs(want) + 1e-6 * np.abs(g).max())
+    else:
+        assert rel_fro(got, want) <= 1e-5
+        assert np.abs(got - want).max(initial=0) <= 1e-6 * max(1.0, np.abs(g).max())
+
+
+@pytest.mark.parametrize("s,V,t,bf16", [(33, 1024, 4, False), (33, 1024, 4, True), (17, 24, 8, False),
+                                        (5, 9, 9, False), (64, 16032 * 2, 2, True), (7, 4004, 4, False),
+                                        (1, 40, 1, True)])
+def test_ce_bwd_shards(oracle_mod, s, V, t, bf16):
+    """Every shard's gradient slice against the oracle, from the combined
+    (M, S) of the oracle's own shard statistics (rounded to fp32 as the GPU
+    receives them); the slices concatenate to the full-vocabulary gradient."""
+    rng = np.random.default_rng(s * 31 + V)
+    z = (rng.standard_normal((s, V)) * 3).astype(np.float32)
+    y = rng.integers(0, V, s).astype(np.int64)
+    if s > 3:
+        y[:3] = [0, V - 1, V + 5]   # first id, last id, an id beyond the vocabulary
+    g = rng.standard_normal(s).astype(np.float32)
+    Vs = V // t
+    st = [oracle_mod.ce_stats(z[:, i * Vs:(i + 1) * Vs], y, i * Vs) for i in range(t)]
+    M, S = oracle_mod.ce_global([a[0] for a in st], [a[1] for a in st])
+    M32, S32 = M.astype(np.float32), S.astype(np.float32)
+    full = []
+    for i in range(t):
+        zi = np.ascontiguousarray(z[:, i * Vs:(i + 1) * Vs])
+        got = run_ce_bwd(zi, y, i * Vs, M32, S32, g, bf16)
+        want = oracle_mod.ce_bwd(zi, y, i * Vs, M32, S32, g)
+        check_ce_bwd(got, want, g, bf16)
+        full.append(got)
+    if not bf16:
+        # softmax sums to 1: each full row sums to g * (1 - [target in vocabulary])
+        rows = np.concatenate(full, axis=1).sum(axis=1)
+        in_v = (y >= 0) & (y < V)
+        np.testing.assert_allclose(rows, np.where(in_v, 0.0, g), atol=2e-5 * max(1.0, np.abs(g).max()))
+
+
+def test_ce_bwd_vocab_shard(oracle_mod):
+    """The [8192, 16032] logit slice of shard 0, fp32 and bf16 gradients, on
+    sampled rows, with (M, S) those of a one-shard vocabulary."""
+    d = I.vocab_inputs(5, shards=[0], with_lm=False, with_table=False)
+    z, y = d["logits"][0], d["targets"]
+    m, se, _ = oracle_mod.ce_stats(z, y, 0)
+    M32, S32 = m.astype(np.float32), se.astype(np.float32)
+    g = np.full(d["s"], 1.0 / d["s"], np.float32)
+    rows = I.sample_rows(d["s"], 64, 5, 23)
+    for bf16 in (False, True):
+        got = run_ce_bwd(z, y, 0, M32, S32, g, bf16)
+        want = oracle_mod.ce_bwd(z[rows], y[rows], 0, M32[rows], S32[rows], g[rows])
+        check_ce_bwd(got[rows], want, g, bf16)
+        assert np.all(np.isfinite(got))
 
 
 # ---------------------------------------------------------------- embedding
