@@ -46,6 +46,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a 1 GiB device-to-device copy (HBM counter calibration)")
+    p.add_argument("--traffic-summary", default=None, metavar="DIR",
+                   help="reduce rocprofv3 FETCH_SIZE/WRITE_SIZE passes under DIR to profiles/hbm_traffic.json")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU time of the oracle sample")
     return p.parse_args()
@@ -272,8 +274,66 @@ def traffic_for(kernel_key: str):
     return e["bytes_per_launch"]
 
 
+# Kernels whose HBM traffic the counter passes measure: summary key -> (pass
+# directory prefix, kernel-name substring, sources the kernel is built from,
+# algorithmic bytes per launch at the V=128256 t=8 vocab shard, s = h = 8192).
+_S5, _H5, _V5 = 8192, 8192, 16032
+TRAFFIC_KERNELS = {
+    "lm_head_gemm": ("lm", "gemm_dma_kernel<256, 256, true, false, 0, true, false>",
+                     ["gemm_bf16_kernels.h", "gemm_bf16.hip", "gemm_desc.h"],
+                     2 * _S5 * _H5 + 2 * _H5 * _V5 + 4 * _S5 * _V5),
+    "lm_head_ce_gemm": ("lmce", "gemm_dma_kernel<256, 256, true, false, 6, true, false>",
+                        ["gemm_bf16_kernels.h", "gemm_bf16.hip", "gemm_desc.h"],
+                        2 * _S5 * _H5 + 2 * _H5 * _V5 + 8 * _S5),
+    "vocab_ce": ("ce", "vocab_ce_kernel<4>", ["vocab.hip"], 4 * _S5 * _V5 + 8 * _S5 + 12 * _S5),
+    "vocab_ce_bwd": ("cebwd", "vocab_ce_bwd_kernel<4, true>", ["vocab.hip"],
+                     4 * _S5 * _V5 + 2 * _S5 * _V5 + 8 * _S5 + 12 * _S5),
+}
+
+
+def summarize_traffic(d: str):
+    """Reduce the rocprofv3 FETCH_SIZE / WRITE_SIZE passes under `d` (one pass
+    per directory <prefix>_<COUNTER>, plus copy_<COUNTER> for the 1 GiB copy)
+    to profiles/hbm_traffic.json: the copy calibrates each counter (bytes per
+    KiB reported), then each kernel's mean counter per dispatch is scaled."""
+    import csv
+    import glob
+
+    def mean_counter(prefix, counter, needle):
+        vals = []
+        for f in glob.glob(os.path.join(d, f"{prefix}_{counter}", "**", "*counter_collection.csv"),
+                           recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    if r["Counter_Name"] == counter and needle in r["Kernel_Name"]:
+                        vals.append(float(r["Counter_Value"]))
+        return sum(vals) / len(vals) if vals else None
+
+    copy_bytes = 1 << 30
+    cf = mean_counter("copy", "FETCH_SIZE", "copyBuffer")
+    cw = mean_counter("copy", "WRITE_SIZE", "copyBuffer")
+    out = {"calibration": {"copy_bytes": copy_bytes, "fetch_size_kb": cf, "write_size_kb": cw,
+                           "fetch_factor": round(copy_bytes / (cf * 1024), 4),
+                           "write_factor": round(copy_bytes / (cw * 1024), 4)}}
+    ff, wf = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
+    for key, (prefix, needle, sources, alg) in TRAFFIC_KERNELS.items():
+        f = mean_counter(prefix, "FETCH_SIZE", needle)
+        w = mean_counter(prefix, "WRITE_SIZE", needle)
+        if f is None or w is None:
+            continue
+        out[key] = {"kernel": needle, "sources": sources, "src_hash": src_hash(*sources),
+                    "fetch_size_kb": round(f, 1), "write_size_kb": round(w, 1),
+                    "bytes_per_launch": int(f * 1024 * ff + w * 1024 * wf), "algorithmic_bytes": alg}
+    with open(os.path.join(ROOT, "profiles", "hbm_traffic.json"), "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def main():
     args = parse()
+    if args.traffic_summary:
+        summarize_traffic(args.traffic_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
               file=sys.stderr)
@@ -296,7 +356,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": 1 << 30, "launches": 3}))
         return
-    rows = build_rows(torch, args.rows, args.only if args.only not in ("vocab_ce", "vocab_ce_bwd") else "lm_head_fwd")
+    first = "lm_head_fwd" if args.only in ("vocab_ce", "vocab_ce_bwd") else args.only
+    rows = build_rows(torch, args.rows, first)
     if args.only:
         keep = [r for r in rows if r.name == args.only]
         if not keep:
@@ -368,7 +429,7 @@ def main():
     if "lm_head_fwd" in by:
         r = by["lm_head_fwd"]
         ach = r.flops / (r.ms() * 1e-3) / 1e12
-        res["roofline"] = {"kernel": "gemm_bf16_kernel<256,256,NN,store fp32> (tp_lm_head_fwd)",
+        res["roofline"] = {"kernel": "gemm_dma_kernel<256,256,NN,store fp32> (tp_lm_head_fwd)",
                            "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
                            "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
                            "traffic": traffic_for("lm_head_gemm")}
@@ -380,7 +441,7 @@ def main():
     else:
         r = by["mlp_bwd"]
         ach = r.flops / (r.ms() * 1e-3) / 1e12
-        res["roofline"] = {"kernel": "gemm_bf16_kernel (tp_mlp_bwd, 4 GEMMs)", "bound": "mfma",
+        res["roofline"] = {"kernel": "gemm_dma kernels (tp_mlp_bwd, 4 GEMMs)", "bound": "mfma",
                            "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                            "frac": round(ach / PEAK_BF16_TFLOPS, 4), "traffic": None}
     if not args.no_cpu_baseline:
