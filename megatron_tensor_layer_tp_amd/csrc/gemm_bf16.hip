@@ -23,6 +23,11 @@ hipError_t launch_shape_k(const GemmDesc &d, int bm, int bn, hipStream_t st, boo
     return hipGetLastError();
   }
   if (bm == 256 && bn == 256) return launch_dma<256, 256, A_KC, B_KC, EPI, OUT_F32, KSEG>(d, st);
+  // 192-column tiles: N = 768 or 1536 then fills all 256 CUs (not for the dual or CE epilogues)
+  if constexpr (EPI != EPI_SWIGLU_FWD && EPI != EPI_CE_STATS) {
+    if (bm == 256 && bn == 192) return launch_dma<256, 192, A_KC, B_KC, EPI, OUT_F32, KSEG>(d, st);
+    if (bm == 128 && bn == 192) return launch_dma<128, 192, A_KC, B_KC, EPI, OUT_F32, KSEG>(d, st);
+  }
   if (bm == 256 && bn == 128) return launch_dma<256, 128, A_KC, B_KC, EPI, OUT_F32, KSEG>(d, st);
   if (bm == 128 && bn == 256) return launch_dma<128, 256, A_KC, B_KC, EPI, OUT_F32, KSEG>(d, st);
   return launch_dma<128, 128, A_KC, B_KC, EPI, OUT_F32, KSEG>(d, st);

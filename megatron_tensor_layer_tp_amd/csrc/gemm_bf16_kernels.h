@@ -388,6 +388,9 @@ __device__ __forceinline__ void epilogue(const GemmDesc &d, f32x16 (&acc)[BM / 6
   constexpr int OUTW = DUAL ? WTN / 2 : WTN;        // output columns per strip row
   constexpr int LPR = OUTW / 8;                     // lanes per strip row
   constexpr int RPI = 64 / LPR;                     // strip rows per pass
+  constexpr int NIT = (32 + RPI - 1) / RPI;         // passes per 32-row strip
+  // 96-column strips (192-wide tiles): 12 lanes per row, 5 rows per pass, lanes 60-63 idle
+  static_assert(EPI != EPI_CE_STATS || (64 % LPR == 0 && 32 % RPI == 0), "CE rows span a DPP row");
   const int ci = lane & 31;
   const int rsub = 4 * (lane >> 5);
   const int col_base = n0 + (DUAL ? wn * (BN / 4) : wn * WTN);
@@ -401,8 +404,10 @@ __device__ __forceinline__ void epilogue(const GemmDesc &d, f32x16 (&acc)[BM / 6
         ep[(8 * (e >> 2) + rsub + (e & 3)) * EPS + fn * 32 + ci] = acc[fm][fn][e];
     __syncthreads();
 #pragma unroll 2
-    for (int it = 0; it < 32 / RPI; ++it) {
-      const int r = it * RPI + lane / LPR;
+    for (int it = 0; it < NIT; ++it) {
+      const int r0 = it * RPI + lane / LPR;
+      const bool live = lane < RPI * LPR && r0 < 32;
+      const int r = live ? r0 : 0;
       const int c = (lane % LPR) * 8;
       const float *src = ep + r * EPS + c;
       float x[8], u[8];
@@ -417,7 +422,7 @@ __device__ __forceinline__ void epilogue(const GemmDesc &d, f32x16 (&acc)[BM / 6
       if constexpr (EPI == EPI_CE_STATS) {
         ce_stats8<LPR>(d, gm, gn, nlen, col_base / WTN, lane, x);
       } else {
-        if (gm < d.M && gn < nlen) epi8<EPI, OUT_F32, VEC>(d, gm, gn, nlen, sc, split, x, u);
+        if (live && gm < d.M && gn < nlen) epi8<EPI, OUT_F32, VEC>(d, gm, gn, nlen, sc, split, x, u);
       }
     }
   }
@@ -601,9 +606,11 @@ typedef __attribute__((address_space(3))) char lds_char_t;
 __device__ __forceinline__ int swk(int r) { return (r & 7) ^ ((r >> 3) & 3); }
 // row-contiguous tiles [64 k][C*8]: chunk c of k-row k sits at c ^ swr(k); the
 // 4 k-rows x 32 columns read by half a wave's transpose loads land on 16
-// distinct 16-byte bank groups.
+// distinct 16-byte bank groups.  With 24 chunks (192 columns, 384-byte k-rows,
+// which alternate between the two 128-byte halves of the bank array) flipping
+// chunk bit 2 on every other pair of k-rows is enough, and it keeps c < 24.
 template <int C>
-__device__ __forceinline__ int swr(int k) { return C >= 16 ? 4 * (k & 3) : 4 * ((k >> 1) & 1); }
+__device__ __forceinline__ int swr(int k) { return (C == 16 || C == 32) ? 4 * (k & 3) : 4 * ((k >> 1) & 1); }
 
 // buffer resource words for a wave-uniform base pointer
 __device__ __forceinline__ i32x4 rsrc_words(const void *p) {
@@ -643,9 +650,8 @@ struct Dma {
   static constexpr int NI = R / 32;
   static constexpr int REFF = DUAL ? R / 2 : R;   // columns of one row-contiguous sub-tile
   static constexpr int P = 2 * REFF;              // its k-row pitch (bytes)
-  static constexpr int KPB = KC ? 8 : 1024 / P;   // rows / k-rows per kilobyte
   uint32_t vo[NI];   // per-lane byte offset within the block
-  uint32_t so[NI];   // wave-uniform byte offset of the block
+  uint32_t so[NI];   // wave-uniform byte offset of the block's first row / k-row
   int extent;        // rows (KC) or columns (RC) from the tile origin to the matrix edge
   __device__ __forceinline__ int blk(int wave, int i) const {
     const int b = wave * NI + i;
@@ -656,15 +662,18 @@ struct Dma {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int bl = blk(wave, i);
-      so[i] = (uint32_t)__builtin_amdgcn_readfirstlane((int)(bl * KPB * ld * 2));
       if constexpr (KC) {
+        so[i] = (uint32_t)__builtin_amdgcn_readfirstlane((int)(bl * 8 * ld * 2));
         const int r = 8 * bl + (lane >> 3);
         const int c = (lane & 7) ^ swk(r);
         vo[i] = (uint32_t)((lane >> 3) * ld * 2 + c * 16);
       } else {
-        const int k = (bl * 1024 + lane * 16) / P;
-        const int c = ((lane * 16) % P / 16) ^ swr<REFF / 8>(k);
-        vo[i] = (uint32_t)((k - bl * KPB) * ld * 2 + c * 16);
+        // the kilobyte may start inside a k-row (P = 384)
+        const int q = bl * 1024 + lane * 16, kf = bl * 1024 / P;
+        const int k = q / P;
+        const int c = (q % P / 16) ^ swr<REFF / 8>(k);
+        so[i] = (uint32_t)__builtin_amdgcn_readfirstlane((int)(kf * ld * 2));
+        vo[i] = (uint32_t)((k - kf) * ld * 2 + c * 16);
       }
     }
   }
@@ -682,8 +691,9 @@ struct Dma {
           const int c = (lane & 7) ^ swk(r);
           if (r >= extent || c * 8 >= kleft) o[i] = OOB;
         } else {
-          const int k = (bl * 1024 + lane * 16) / P;
-          const int c = ((lane * 16) % P / 16) ^ swr<REFF / 8>(k);
+          const int q = bl * 1024 + lane * 16;
+          const int k = q / P;
+          const int c = (q % P / 16) ^ swr<REFF / 8>(k);
           if (k >= kleft || c * 8 >= extent) o[i] = OOB;
         }
       }
@@ -702,7 +712,7 @@ __device__ __forceinline__ int rc_frag_off(int P, int C, int col0, int h, int la
   const int g = (lane >> 4) & 3, j = lane & 15;
   const int col = col0 + 16 * (g & 1) + 4 * (j & 3);
   const int k = 8 * (g >> 1) + (j >> 2) + 4 * h;
-  const int sw = C >= 16 ? 4 * (k & 3) : 4 * ((k >> 1) & 1);
+  const int sw = (C == 16 || C == 32) ? 4 * (k & 3) : 4 * ((k >> 1) & 1);
   return k * P + (((col >> 3) ^ sw) << 4) + ((col & 7) << 1);
 }
 __device__ __forceinline__ bf16x8 read_tr(const char *p0, const char *p1) {

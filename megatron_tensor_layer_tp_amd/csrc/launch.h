@@ -10,7 +10,8 @@ enum GemmLayout : int {
   GEMM_TN = 2,  // A [K][M], B [K][N]
 };
 
-// bf16 MFMA tiles: bm, bn in {128, 256}; vec = 16-byte loads are legal for
+// bf16 MFMA tiles: bm in {128, 256}, bn in {128, 192, 256} (192 not for the
+// dual or CE-statistics epilogues); vec = 16-byte loads are legal for
 // every operand (aligned pointers, leading dimensions and extents multiple of 8).
 hipError_t tp_launch_gemm_bf16(const GemmDesc &d, int layout, int epi, bool out_f32, int bm, int bn,
                                bool vec, hipStream_t st);
@@ -27,6 +28,9 @@ struct GemmVariant {
 };
 hipError_t tp_launch_gemm_pair(const GemmDesc &d1, const GemmVariant &v1, const GemmDesc &d2,
                                const GemmVariant &v2, bool dry, hipStream_t st);
+// the pairs whose first product is a TN split-K partial (called by tp_launch_gemm_pair)
+hipError_t tp_launch_gemm_pair_tn_partial(const GemmDesc &d1, const GemmVariant &v1, const GemmDesc &d2,
+                                          const GemmVariant &v2, bool dry, hipStream_t st);
 
 // fp32 storage and arithmetic (64x64 tiles, any layout, any extents).
 constexpr int TP_F32_TILE = 64;

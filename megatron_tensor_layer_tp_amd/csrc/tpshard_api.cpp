@@ -116,6 +116,7 @@ struct Spec {               // one product, described before planning
   bool dual = false;
   bool can_split = false;   // a workspace for split-K partials is available
   bool bm256 = false;       // only 256-row tiles (the shapes built for paired launches)
+  bool no192 = false;       // no 192-column tiles
   int64_t seg[TP_MAX_SEG] = {0, 0, 0};  // N-extents (N-segments) or K-extents (K-segments)
   int64_t N = 0;            // total N (kseg or single segment)
   int64_t lds[12] = {};     // every leading dimension involved
@@ -140,12 +141,16 @@ int64_t ktiles(const Spec &s) {
   return t;
 }
 
-// Relative MFMA efficiency of each tile shape (larger tiles re-read less and
-// keep the LDS traffic per MFMA lower); 128x128 runs two workgroups per CU.
-double tile_eff(int bm, int bn) {  // measured on MI355X, relative to 256x256
+// Relative MFMA efficiency of each tile shape per FLOP (larger tiles re-read
+// less and keep the LDS traffic per MFMA lower); 128x128 runs two workgroups
+// per CU.  Measured on MI355X in full rounds of an 8192x8192x3584 product,
+// relative to 256x256.
+double tile_eff(int bm, int bn) {
   if (bm == 256 && bn == 256) return 1.0;
+  if (bm == 256 && bn == 192) return 0.9;
+  if (bm == 128 && bn == 192) return 0.65;
   if (bm == 128 && bn == 128) return 0.53;
-  return 0.78;
+  return 0.78;  // 256x128, 128x256
 }
 
 Plan plan_bf16(const Spec &s) {
@@ -165,12 +170,15 @@ Plan plan_bf16(const Spec &s) {
   p.vec = vec;
   const int64_t KT = ktiles(s);
   const bool can_split = s.can_split && s.epi == EPI_STORE && !s.dual && KT >= 8;
-  static const int shapes[4][2] = {{256, 256}, {256, 128}, {128, 256}, {128, 128}};
+  // 192 columns: N = 768, 1536 or 6144 then fills the 256 CUs in whole rounds
+  static const int shapes[6][2] = {{256, 256}, {256, 192}, {256, 128}, {128, 256}, {128, 192}, {128, 128}};
+  const bool no192 = s.no192 || s.dual || s.epi == EPI_CE_STATS;
   double best = 1e300;
   for (auto &sh : shapes) {
     const int bm = sh[0], bn = sh[1];
     if (!vec && !(bm == 128 && bn == 128)) continue;
     if (s.bm256 && bm != 256) continue;
+    if (no192 && bn == 192) continue;
     const int64_t tm = cdiv(s.M, bm), tn = ntiles_n(s, bn);
     const int64_t tiles = tm * tn;
     const int slots = (bm == 128 && bn == 128) ? 2 * kCUs : kCUs;
@@ -327,6 +335,10 @@ PairPlan pair_plan(const Spec &s1, const Spec &s2, int dt) {
     Spec a = s1, b = s2;
     a.bm256 = b.bm256 = true;
     b.can_split = false;
+    // 192-column tiles are built for TN first products and for NT stores / activation
+    // backward as the second
+    a.no192 = a.layout != GEMM_TN || a.kseg;
+    b.no192 = b.layout != GEMM_NT || b.kseg || (b.epi != EPI_STORE && b.epi != EPI_ACT_BWD);
     r.p1 = plan_bf16(a);
     r.p2 = plan_bf16(b);
     GemmDesc d1, d2;
