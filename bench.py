@@ -80,8 +80,65 @@ class Row:
         else:
             self.fn()
 
+    def times(self):
+        return sorted(a.elapsed_time(b) for a, b in self.events)
+
     def ms(self):
         return sum(a.elapsed_time(b) for a, b in self.events) / max(1, len(self.events))
+
+    def pct(self, q):
+        t = self.times()
+        return t[min(len(t) - 1, int(q * (len(t) - 1) + 0.5))] if t else 0.0
+
+
+class GpuSampler:
+    """Best-effort shader clock and temperature of the GPU during the timed
+    steps, read from the amdgpu hwmon files in sysfs (read-only); empty when
+    the files are not there."""
+
+    def __init__(self):
+        import glob
+        import threading
+        self.files = {}
+        for hw in sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*")):
+            f = os.path.join(hw, "freq1_input")
+            if os.path.exists(f):
+                self.files["sclk_mhz"] = (f, 1e-6)
+                for t in sorted(glob.glob(os.path.join(hw, "temp*_input"))):
+                    lab = t.replace("_input", "_label")
+                    name = open(lab).read().strip() if os.path.exists(lab) else os.path.basename(t)[:-6]
+                    self.files[f"temp_{name}_c"] = (t, 1e-3)
+                break
+        self.samples = {k: [] for k in self.files}
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        while not self._stop.is_set():
+            for k, (f, scale) in self.files.items():
+                try:
+                    with open(f) as fh:
+                        self.samples[k].append(float(fh.read()) * scale)
+                except (OSError, ValueError):
+                    pass
+            self._stop.wait(0.01)
+
+    def __enter__(self):
+        if self.files:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self.files:
+            self._thread.join()
+
+    def summary(self):
+        out = {}
+        for k, v in self.samples.items():
+            if v:
+                out[k] = {"mean": round(sum(v) / len(v), 1), "max": round(max(v), 1), "n": len(v)}
+        return out or None
 
 
 def build_rows(torch, which, only=None):
@@ -373,12 +430,13 @@ def main():
         for r in rows:
             r.run(torch, False)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        for r in rows:
-            r.run(torch, True)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with GpuSampler() as sampler:
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            for r in rows:
+                r.run(torch, True)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
 
     by = {r.name: r for r in rows}
     if args.only:
@@ -394,7 +452,8 @@ def main():
     out_rows = {}
     for r in rows:
         ms = r.ms()
-        e = {"config": r.config, "ms": round(ms, 4)}
+        e = {"config": r.config, "ms": round(ms, 4), "ms_p10": round(r.pct(0.1), 4),
+             "ms_median": round(r.pct(0.5), 4), "ms_p90": round(r.pct(0.9), 4)}
         if r.flops:
             tf = r.flops / (ms * 1e-3) / 1e12
             e.update(tflops=round(tf, 2), frac_mfma_peak=round(tf / PEAK_BF16_TFLOPS, 4))
@@ -422,6 +481,7 @@ def main():
                                 "(llama3-70b t=8, s=8192); lm head + vocab CE + embedding "
                                 "(V=128256 t=8, s=8192)" if args.rows == "all" else "mlp fwd+bwd only"},
         "rows": out_rows,
+        "gpu_during_steps": sampler.summary(),
     }
     if "vocab_ce" in by:
         ce = by["vocab_ce"]
