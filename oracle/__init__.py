@@ -59,6 +59,8 @@ def _L():
         lib.or_ce_combine.argtypes = [_i64, _i64, _d, _d, _d, _d]
         lib.or_ce_direct.argtypes = [_i64, _i64, _d, ctypes.c_void_p, _d]
         lib.or_ce_bwd.argtypes = [_i64, _i64, _i64, _d, ctypes.c_void_p, _d, _d, _d, _d]
+        lib.or_attn_fwd.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, _d, _d, _d, _i64, ctypes.c_void_p,
+                                    _d, _d]
         lib.or_embed_u16.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_void_p,
                                      ctypes.c_void_p, ctypes.c_void_p]
         lib.or_embed_u32.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_void_p,
@@ -370,3 +372,28 @@ def embed(ids, table, vocab_start: int):
         else:
             raise TypeError("table elements must be 2 or 4 bytes")
     return out
+
+
+# ---------------------------------------------------------------------------
+# attention core on the shard's heads
+# [book] §7.3.4 (each card runs attention on its own 8 query heads and 1 KV
+# head, then concatenates them to [s, 1024]); the CS336 lecture-8 book's
+# activation-memory section (FlashAttention recomputes the s x s scores)
+# ---------------------------------------------------------------------------
+def attn_fwd(Q, K, V, nq: int, nkv: int, causal: bool = True, rows=None):
+    """O = softmax(Q_j K_g^T / sqrt(d) + causal mask) V_g for every query head j
+    (KV head g = j // (nq // nkv)), and the per-head log-sum-exp of the scores.
+    Q [s, nq*d], K and V [s, nkv*d]; returns O [len(rows), nq*d] and lse
+    [nq, len(rows)] (all positions when rows is None)."""
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    s = Q.shape[0]
+    d = Q.shape[1] // nq
+    assert Q.shape[1] == nq * d and K.shape == (s, nkv * d) and V.shape == K.shape and nq % nkv == 0
+    rows = np.arange(s, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    nr = rows.shape[0]
+    O = np.empty((nr, nq * d))
+    lse = np.empty((nq, nr))
+    if nr and d:
+        _L().or_attn_fwd(s, nq, nkv, d, int(bool(causal)), _p(Q), _p(K), _p(V), nr, rows.ctypes.data,
+                         _p(O), _p(lse))
+    return O, lse

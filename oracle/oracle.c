@@ -24,6 +24,7 @@
  *    book §7.3.4 and lecture 16 notes §5.5.
  */
 #include <math.h>
+#include <stdlib.h>
 #include <stdint.h>
 #include <stddef.h>
 
@@ -216,3 +217,49 @@ void or_embed_u32(int64_t n, int64_t Vs, int64_t h, int64_t start,
 }
 
 int or_version(void) { return 1; }
+
+/* ---------------------------------------------------------------------- */
+/* attention core on the shard's heads                                     */
+/* ---------------------------------------------------------------------- */
+
+/* Causal scaled dot-product attention of the nq query heads a shard holds,
+ * sharing nkv key/value heads (query head j reads KV head j / (nq / nkv)).
+ * Q [s][nq*d], K and V [s][nkv*d], row-major with head j in columns
+ * [j*d, (j+1)*d).  For every head j and each of the nr positions r = rows[i]:
+ *   S[c]   = (Q_j[r] . K_g[c]) / sqrt(d)          for c = 0..r (causal)
+ *   lse    = m + ln sum_c exp(S[c] - m),  m = max_c S[c]
+ *   O_j[r] = sum_c exp(S[c] - lse) V_g[c]
+ * written to O [nr][nq*d] and lse [nq][nr].  With causal = 0 every c in
+ * 0..s-1 is visible. */
+void or_attn_fwd(int64_t s, int64_t nq, int64_t nkv, int64_t d, int causal, const double *Q,
+                 const double *K, const double *V, int64_t nr, const int64_t *rows, double *O,
+                 double *lse)
+{
+    const int64_t grp = nq / nkv, lq = nq * d, lk = nkv * d;
+    const double scale = 1.0 / sqrt((double)d);
+    #pragma omp parallel for schedule(dynamic) collapse(2)
+    for (int64_t j = 0; j < nq; ++j) {
+        for (int64_t i = 0; i < nr; ++i) {
+            const int64_t r = rows[i], g = j / grp;
+            const int64_t n = causal ? r + 1 : s;
+            double *S = (double *)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+            double m = -INFINITY;
+            for (int64_t c = 0; c < n; ++c) {
+                double acc = 0.0;
+                for (int64_t k = 0; k < d; ++k) acc += Q[r * lq + j * d + k] * K[c * lk + g * d + k];
+                S[c] = acc * scale;
+                if (S[c] > m) m = S[c];
+            }
+            double sum = 0.0;
+            for (int64_t c = 0; c < n; ++c) sum += exp(S[c] - m);
+            const double L = m + log(sum);
+            lse[j * nr + i] = L;
+            for (int64_t k = 0; k < d; ++k) {
+                double acc = 0.0;
+                for (int64_t c = 0; c < n; ++c) acc += exp(S[c] - L) * V[c * lk + g * d + k];
+                O[i * lq + j * d + k] = acc;
+            }
+            free(S);
+        }
+    }
+}
