@@ -169,7 +169,7 @@ def build_rows(torch, which, only=None):
         rows += mlp_rows(torch, up, bf, I, T)
     if which == "mlp":
         return rows
-    if want("swiglu_fwd", "swiglu_bwd", "attn_proj_fwd", "attn_proj_bwd"):
+    if want("swiglu_fwd", "swiglu_bwd", "attn_proj_fwd", "attn_proj_bwd", "attn_core_fwd"):
         rows += layer_rows(torch, up, bf, I, T, want)
     if want("lm_head_fwd", "vocab_ce", "vocab_embed", "vocab_ce_bwd", "lm_head_ce_fused"):
         rows += vocab_rows(torch, up, bf, I, T)
@@ -225,6 +225,15 @@ def layer_rows(torch, up, bf, I, T, want):
     Q, K, V = bf((s4, dq)), bf((s4, dkv)), bf((s4, dkv))
     dWq, dWk, dWv, dO, dWo = bf((h4, dq)), bf((h4, dkv)), bf((h4, dkv)), bf((s4, dq)), bf((dq, h4))
     Ya = bf((s4, h4))
+    # attention core between the projections: causal, 8 query heads on 1 KV head, d = 128
+    ac = I.attn_core_inputs(4)
+    Qc, Kc, Vc = up(ac["Q"][0]), up(ac["K"][0]), up(ac["V"][0])
+    nqc, nkvc = ac["nq"], ac["nkv"]
+    Oc = bf((s4, dq))
+    lsec = torch.empty((nqc, s4), dtype=torch.float32, device=dev)
+    del ac
+    rows.append(Row("attn_core_fwd", c4, lambda: T.tp_attn_core_fwd(BF, s4, nqc, nkvc, 128, Qc, Kc, Vc, Oc, lsec),
+                    flops=2.0 * 2.0 * (s4 * (s4 + 1) / 2.0) * 128 * nqc))
     nba = T.tp_attn_proj_bwd_workspace(BF, s4, h4, dq, dkv)
     wsa = torch.empty(max(nba, 256), dtype=torch.uint8, device=dev)
     qkv = 2.0 * s4 * h4 * (dq + 2 * dkv)

@@ -161,6 +161,21 @@ int tp_attn_proj_bwd(int dt, int64_t s, int64_t h, int64_t dq, int64_t dkv,
                      void *dX, void *dWq, void *dWk, void *dWv, void *dO, void *dWo,
                      void *ws, size_t ws_bytes, void *stream);
 
+/* Attention core on the shard's heads ([book] §7.3.4: each card runs attention
+ * on its own query heads -- 8 of Llama-3-70B's 64 at t = 8 -- which share its
+ * key/value heads, 1 of 8; the outputs concatenate to [s, nq*d], the input of
+ * the row-split W_O product).  Causal scaled dot-product attention:
+ *     S = Q_j K_g^T / sqrt(d) over keys c <= r,  O_j[r] = softmax(S) V_g,
+ *     lse[j][r] = ln sum_c exp(S[r][c]),
+ * query head j reading KV head g = j / (nq / nkv).  Q [s][nq*d], K and V
+ * [s][nkv*d], O [s][nq*d] (head j in columns [j*d, (j+1)*d)), lse [nq][s]
+ * fp32.  dt must be TP_DT_BF16 and d = 128 (TP_EUNSUPPORTED otherwise); nq
+ * must be a multiple of nkv (TP_ESHAPE).  Flash-style: the s x s scores are
+ * never stored; P is rounded to bf16 before the product with V. */
+int tp_attn_core_fwd(int dt, int64_t s, int64_t nq, int64_t nkv, int64_t d,
+                     const void *Q, const void *K, const void *V, void *O, float *lse,
+                     void *stream);
+
 /* ------------------------------------------------------------------------ */
 /* Vocab-parallel output layer, cross entropy and embedding                   */
 /* ([book] §7.3.4; [lec16] §5.5)                                              */

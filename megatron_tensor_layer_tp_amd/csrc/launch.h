@@ -46,3 +46,7 @@ hipError_t tp_launch_ce_merge(const float *ws, int P, int W, int64_t s, int64_t 
                               const int64_t *tgt, float *m, float *se, float *tl, hipStream_t st);
 hipError_t tp_launch_vocab_embed(int elem_bytes, int64_t n, int64_t Vs, int64_t h, int64_t start,
                                  const int64_t *ids, const void *table, void *out, hipStream_t st);
+
+// causal attention core, head dim 128, bf16 Q [s][nq*128], K/V [s][nkv*128], O like Q, lse [nq][s]
+hipError_t tp_launch_attn_fwd(int64_t s, int64_t nq, int64_t nkv, const void *Q, const void *K, const void *V,
+                              void *O, float *lse, hipStream_t st);

@@ -902,6 +902,24 @@ int tp_vocab_ce_bwd(int dt, int64_t s, int64_t Vs, int64_t vocab_start, const fl
   return ok();
 }
 
+int tp_attn_core_fwd(int dt, int64_t s, int64_t nq, int64_t nkv, int64_t d, const void *Q, const void *K,
+                     const void *V, void *O, float *lse, void *stream) {
+  Checker c;
+  int64_t nqe, nke, nl;
+  c.dtype(dt, false, "tp_attn_core_fwd");
+  c.dim(s, "s") && c.dim(nq, "nq") && c.dim(nkv, "nkv") && c.dim(d, "d");
+  if (!c.status && d != 128) c.status = fail(TP_EUNSUPPORTED, "tp_attn_core_fwd: head dim %lld (only 128)", (long long)d);
+  if (!c.status && nq > 0 && (nkv == 0 || nq % nkv != 0))
+    c.status = fail(TP_ESHAPE, "tp_attn_core_fwd: nq = %lld is not a multiple of nkv = %lld", (long long)nq,
+                    (long long)nkv);
+  c.elems(s, nq * d, nqe, "Q") && c.elems(s, nkv * d, nke, "K") && c.elems(nq, s, nl, "lse");
+  c.ptr(Q, nqe, "Q") && c.ptr(K, nke, "K") && c.ptr(V, nke, "V") && c.ptr(O, nqe, "O") && c.ptr(lse, nl, "lse");
+  if (c.status) return c.status;
+  hipError_t e = tp_launch_attn_fwd(s, nq, nkv, Q, K, V, O, lse, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TP_EHIP, "tp_attn_core_fwd: %s", hipGetErrorString(e));
+  return ok();
+}
+
 size_t tp_lm_head_ce_workspace(int dt, int64_t s, int64_t h, int64_t Vs) {
   Checker c;
   c.dtype(dt, false, "tp_lm_head_ce_workspace");

@@ -26,6 +26,7 @@ ENTROPY = 20261202
 # tensor ids used in the seed key; never renumber (stored values depend on them)
 T_X, T_W1, T_W2, T_DY, T_WG, T_WU, T_WD, T_WQ, T_WK, T_WV, T_WO, T_O, T_DQ, T_DK, \
     T_DV, T_HF, T_WLM, T_TGT, T_TABLE, T_IDS, T_LOGITS = range(21)
+T_AQ, T_AK, T_AV = 21, 22, 23   # attention-core inputs
 
 
 def _rng(config: int, tensor: int, shard: int = 0) -> np.random.Generator:
@@ -185,6 +186,20 @@ def attn_inputs(cfg_id: int = 4, shards=(0,), s=None, h=None, dq=None, dkv=None)
     for name, tid, shp in (("O", T_O, (s, dq)), ("dQ", T_DQ, (s, dq)),
                            ("dK", T_DK, (s, dkv)), ("dV", T_DV, (s, dkv))):
         out[name] = {i: normal_bf16(shp, 1.0, cfg_id, tid, i) for i in shards}
+    return out
+
+
+def attn_core_inputs(cfg_id: int = 4, shards=(0,), s=None):
+    """Attention-core shard inputs (bf16 bits): Q [s,dq] (dq / 128 query heads)
+    and K, V [s,dkv] (dkv / 128 key/value heads), N(0,1) draws, so the scores
+    Q.K/sqrt(128) have unit spread."""
+    c = CONFIGS[cfg_id]
+    s = c["s"] if s is None else s
+    dq = shard_width(c["dq_full"], c["t"])
+    dkv = shard_width(c["dkv_full"], c["t"])
+    out = {"s": s, "dq": dq, "dkv": dkv, "nq": dq // 128, "nkv": dkv // 128}
+    for name, tid, w in (("Q", T_AQ, dq), ("K", T_AK, dkv), ("V", T_AV, dkv)):
+        out[name] = {i: normal_bf16((s, w), 1.0, cfg_id, tid, i) for i in shards}
     return out
 
 

@@ -37,6 +37,7 @@ _SIGS = {
     "tp_lm_head_fwd": (_int, [_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
     "tp_vocab_ce": (_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
     "tp_vocab_ce_bwd": (_int, [_int, _i64, _i64, _i64] + [_vp] * 6 + [_vp]),
+    "tp_attn_core_fwd": (_int, [_int, _i64, _i64, _i64, _i64] + [_vp] * 5 + [_vp]),
     "tp_lm_head_ce_workspace": (_sz, [_int, _i64, _i64, _i64]),
     "tp_lm_head_ce_fwd": (_int, [_int, _i64, _i64, _i64, _i64] + [_vp] * 6 + [_vp, _sz, _vp]),
     "tp_vocab_embed": (_int, [_int, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
@@ -163,6 +164,11 @@ def tp_attn_proj_bwd(dt, s, h, dq, dkv, X, Wq, Wk, Wv, O, Wo, dQ, dK, dV, dY, dX
 # ---------------------------------------------------------------- vocab
 def tp_lm_head_fwd(dt, s, h, Vs, Hf, Wlm, logits, stream=None):
     return _call("tp_lm_head_fwd", dt, s, h, Vs, _ptr(Hf), _ptr(Wlm), _ptr(logits), _stream(stream))
+
+
+def tp_attn_core_fwd(dt, s, nq, nkv, d, Q, K, V, O, lse, stream=None):
+    return _call("tp_attn_core_fwd", dt, s, nq, nkv, d, _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(lse),
+                 _stream(stream))
 
 
 def tp_vocab_ce_bwd(dt, s, Vs, vocab_start, logits, target, gmax, gsum, dloss, dlogits, stream=None):

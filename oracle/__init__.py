@@ -380,7 +380,7 @@ def embed(ids, table, vocab_start: int):
 # head, then concatenates them to [s, 1024]); the CS336 lecture-8 book's
 # activation-memory section (FlashAttention recomputes the s x s scores)
 # ---------------------------------------------------------------------------
-def attn_fwd(Q, K, V, nq: int, nkv: int, causal: bool = True, rows=None):
+def attn_core_fwd(Q, K, V, nq: int, nkv: int, causal: bool = True, rows=None):
     """O = softmax(Q_j K_g^T / sqrt(d) + causal mask) V_g for every query head j
     (KV head g = j // (nq // nkv)), and the per-head log-sum-exp of the scores.
     Q [s, nq*d], K and V [s, nkv*d]; returns O [len(rows), nq*d] and lse

@@ -34,7 +34,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     raw = ctypes.CDLL(T.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -161,3 +161,24 @@ def test_vocab_ce_bwd_validation(L):
     assert _st(L, "tp_vocab_ce_bwd", *bad) == T.TP_EALIGN
     # nothing to compute: an empty shard
     assert _st(L, "tp_vocab_ce_bwd", T.TP_DT_BF16, 16, 0, 0, None, A16, A16, A16, A16, None, None) == T.TP_OK
+
+
+def test_attn_core_validation(L):
+    args = [T.TP_DT_BF16, 64, 8, 1, 128] + [A16] * 5 + [None]
+    bad = list(args)
+    bad[4] = 64
+    assert _st(L, "tp_attn_core_fwd", *bad) == T.TP_EUNSUPPORTED
+    bad = list(args)
+    bad[0] = T.TP_DT_F32
+    assert _st(L, "tp_attn_core_fwd", *bad) == T.TP_EUNSUPPORTED
+    bad = list(args)
+    bad[3] = 3
+    assert _st(L, "tp_attn_core_fwd", *bad) == T.TP_ESHAPE
+    bad = list(args)
+    bad[9] = None  # lse
+    assert _st(L, "tp_attn_core_fwd", *bad) == T.TP_EINVAL
+    bad = list(args)
+    bad[8] = A16 + 2
+    assert _st(L, "tp_attn_core_fwd", *bad) == T.TP_EALIGN
+    # nothing to compute: no positions
+    assert _st(L, "tp_attn_core_fwd", T.TP_DT_BF16, 0, 8, 1, 128, None, None, None, None, None, None) == T.TP_OK
