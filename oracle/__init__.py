@@ -59,6 +59,10 @@ def _L():
         lib.or_ce_combine.argtypes = [_i64, _i64, _d, _d, _d, _d]
         lib.or_ce_direct.argtypes = [_i64, _i64, _d, ctypes.c_void_p, _d]
         lib.or_ce_bwd.argtypes = [_i64, _i64, _i64, _d, ctypes.c_void_p, _d, _d, _d, _d]
+        lib.or_sp_ln_fwd.argtypes = [_i64, _i64, ctypes.c_double, ctypes.c_double, _d, _d, ctypes.c_void_p,
+                                     _d, _d, _d, _d, _d, _d]
+        lib.or_sp_ln_bwd.argtypes = [_i64, _i64, ctypes.c_double, _d, _d, _d, _d, _d, _d, ctypes.c_void_p,
+                                     _d, _d, _d, _d]
         lib.or_attn_fwd.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, _d, _d, _d, _i64, ctypes.c_void_p,
                                     _d, _d]
         lib.or_embed_u16.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_void_p,
@@ -397,3 +401,39 @@ def attn_core_fwd(Q, K, V, nq: int, nkv: int, causal: bool = True, rows=None):
         _L().or_attn_fwd(s, nq, nkv, d, int(bool(causal)), _p(Q), _p(K), _p(V), nr, rows.ctypes.data,
                          _p(O), _p(lse))
     return O, lse
+
+
+# ---------------------------------------------------------------------------
+# sequence-parallel region: [book] §7.3.6 (LayerNorm and dropout act on each
+# position independently, so each card keeps only s/t positions between the
+# reduce-scatter that ends a sublayer and the all-gather that starts the next)
+# ---------------------------------------------------------------------------
+LN_EPS = 1e-5
+
+
+def sp_ln_fwd(y, x, mask, gamma, beta, p: float, eps: float = LN_EPS):
+    """u = x + y * mask / (1 - p);  z = LayerNorm(u) * gamma + beta.
+    Returns u, z [n, h] and the per-position mean and 1/sqrt(var + eps)."""
+    y, x, gamma, beta = (_f64(a) for a in (y, x, gamma, beta))
+    mask = np.ascontiguousarray(mask, dtype=np.uint8)
+    n, h = x.shape
+    u, z = np.empty((n, h)), np.empty((n, h))
+    mean, rstd = np.empty(n), np.empty(n)
+    if n and h:
+        _L().or_sp_ln_fwd(n, h, float(p), float(eps), _p(y), _p(x), mask.ctypes.data, _p(gamma), _p(beta),
+                          _p(u), _p(z), _p(mean), _p(rstd))
+    return u, z, mean, rstd
+
+
+def sp_ln_bwd(dz, dun, u, mean, rstd, gamma, mask, p: float):
+    """Gradients of sp_ln_fwd: dx (= du, the residual input), dy (through the
+    dropout), and this slice's dgamma, dbeta."""
+    dz, dun, u, mean, rstd, gamma = (_f64(a) for a in (dz, dun, u, mean, rstd, gamma))
+    mask = np.ascontiguousarray(mask, dtype=np.uint8)
+    n, h = dz.shape
+    dx, dy = np.empty((n, h)), np.empty((n, h))
+    dg, db = np.zeros(h), np.zeros(h)
+    if h:
+        _L().or_sp_ln_bwd(n, h, float(p), _p(dz), _p(dun), _p(u), _p(mean), _p(rstd), _p(gamma),
+                          mask.ctypes.data, _p(dx), _p(dy), _p(dg), _p(db))
+    return dx, dy, dg, db

@@ -263,3 +263,77 @@ void or_attn_fwd(int64_t s, int64_t nq, int64_t nkv, int64_t d, int causal, cons
         }
     }
 }
+
+/* ---------------------------------------------------------------------- */
+/* sequence-parallel region: residual add, dropout and LayerNorm           */
+/* ---------------------------------------------------------------------- */
+
+/* One shard's [n, h] slice of positions (n = s/t) in the region outside the
+ * tensor-parallel sublayers.  y is the sublayer output after the
+ * reduce-scatter, x the residual stream, mask the dropout mask (1 keep, 0
+ * drop) drawn for drop probability p, gamma/beta the LayerNorm parameters:
+ *   u[r]  = x[r] + y[r] * mask[r] / (1 - p)
+ *   mu    = mean_c u[r][c],  var = mean_c (u[r][c] - mu)^2,  rstd = 1/sqrt(var + eps)
+ *   z[r]  = (u[r] - mu) * rstd * gamma + beta
+ * u, z [n][h]; mean, rstd [n]. */
+void or_sp_ln_fwd(int64_t n, int64_t h, double p, double eps, const double *y, const double *x,
+                  const uint8_t *mask, const double *gamma, const double *beta, double *u, double *z,
+                  double *mean, double *rstd)
+{
+    const double keep = 1.0 / (1.0 - p);
+    #pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < n; ++r) {
+        double mu = 0.0;
+        for (int64_t c = 0; c < h; ++c) {
+            const double v = x[r * h + c] + y[r * h + c] * (double)mask[r * h + c] * keep;
+            u[r * h + c] = v;
+            mu += v;
+        }
+        mu /= (double)h;
+        double var = 0.0;
+        for (int64_t c = 0; c < h; ++c) {
+            const double dv = u[r * h + c] - mu;
+            var += dv * dv;
+        }
+        var /= (double)h;
+        const double rs = 1.0 / sqrt(var + eps);
+        mean[r] = mu;
+        rstd[r] = rs;
+        for (int64_t c = 0; c < h; ++c) z[r * h + c] = (u[r * h + c] - mu) * rs * gamma[c] + beta[c];
+    }
+}
+
+/* Backward of the above: dz is the gradient of z, dun the gradient reaching u
+ * along the residual stream from the layer above.  With xh = (u - mu) rstd and
+ * g = dz * gamma:
+ *   du     = dun + rstd * (g - mean_c g - xh * mean_c (g xh))     (LayerNorm backward)
+ *   dx     = du                       (the residual input)
+ *   dy     = du * mask / (1 - p)      (the sublayer output, before the all-gather)
+ *   dgamma = sum_r dz * xh,  dbeta = sum_r dz   (this slice's share) */
+void or_sp_ln_bwd(int64_t n, int64_t h, double p, const double *dz, const double *dun, const double *u,
+                  const double *mean, const double *rstd, const double *gamma, const uint8_t *mask,
+                  double *dx, double *dy, double *dgamma, double *dbeta)
+{
+    const double keep = 1.0 / (1.0 - p);
+    for (int64_t c = 0; c < h; ++c) dgamma[c] = dbeta[c] = 0.0;
+    for (int64_t r = 0; r < n; ++r) {
+        double mg = 0.0, mgx = 0.0;
+        for (int64_t c = 0; c < h; ++c) {
+            const double xh = (u[r * h + c] - mean[r]) * rstd[r];
+            const double g = dz[r * h + c] * gamma[c];
+            mg += g;
+            mgx += g * xh;
+            dgamma[c] += dz[r * h + c] * xh;
+            dbeta[c] += dz[r * h + c];
+        }
+        mg /= (double)h;
+        mgx /= (double)h;
+        for (int64_t c = 0; c < h; ++c) {
+            const double xh = (u[r * h + c] - mean[r]) * rstd[r];
+            const double g = dz[r * h + c] * gamma[c];
+            const double du = dun[r * h + c] + rstd[r] * (g - mg - xh * mgx);
+            dx[r * h + c] = du;
+            dy[r * h + c] = du * (double)mask[r * h + c] * keep;
+        }
+    }
+}
