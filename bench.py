@@ -169,7 +169,8 @@ def build_rows(torch, which, only=None):
         rows += mlp_rows(torch, up, bf, I, T)
     if which == "mlp":
         return rows
-    if want("swiglu_fwd", "swiglu_bwd", "attn_proj_fwd", "attn_proj_bwd", "attn_core_fwd"):
+    if want("swiglu_fwd", "swiglu_bwd", "attn_proj_fwd", "attn_proj_bwd", "attn_core_fwd", "sp_ln_fwd",
+            "sp_ln_bwd"):
         rows += layer_rows(torch, up, bf, I, T, want)
     if want("lm_head_fwd", "vocab_ce", "vocab_embed", "vocab_ce_bwd", "lm_head_ce_fused"):
         rows += vocab_rows(torch, up, bf, I, T)
@@ -234,6 +235,23 @@ def layer_rows(torch, up, bf, I, T, want):
     del ac
     rows.append(Row("attn_core_fwd", c4, lambda: T.tp_attn_core_fwd(BF, s4, nqc, nkvc, 128, Qc, Kc, Vc, Oc, lsec),
                     flops=2.0 * 2.0 * (s4 * (s4 + 1) / 2.0) * 128 * nqc))
+    # sequence-parallel region on this shard's s/t = 1024 positions: residual + dropout + LayerNorm
+    sp = I.sp_inputs(4)
+    n_sp, p_sp = sp["n"], sp["p"]
+    spy, spx, spm, spg, spb, spdz, spdun = (up(sp[k]) for k in ("y", "x", "mask", "gamma", "beta", "dz", "dun"))
+    del sp
+    spu, spz, spdx, spdy = bf((n_sp, h4)), bf((n_sp, h4)), bf((n_sp, h4)), bf((n_sp, h4))
+    spdg, spdb = bf((h4,)), bf((h4,))
+    spmean, sprstd = (torch.empty(n_sp, dtype=torch.float32, device=dev) for _ in range(2))
+    nbs = T.tp_sp_ln_bwd_workspace(BF, n_sp, h4)
+    wss = torch.empty(max(nbs, 256), dtype=torch.uint8, device=dev)
+    el = float(n_sp * h4)
+    rows.append(Row("sp_ln_fwd", c4, lambda: T.tp_sp_ln_fwd(BF, n_sp, h4, p_sp, 1e-5, spy, spx, spm, spg, spb,
+                                                            spu, spz, spmean, sprstd),
+                    bytes_=9.0 * el + 4.0 * h4 + 8.0 * n_sp))
+    rows.append(Row("sp_ln_bwd", c4, lambda: T.tp_sp_ln_bwd(BF, n_sp, h4, p_sp, spdz, spdun, spu, spmean, sprstd,
+                                                            spg, spm, spdx, spdy, spdg, spdb, wss, nbs),
+                    bytes_=11.0 * el + 6.0 * h4 + 8.0 * n_sp))
     nba = T.tp_attn_proj_bwd_workspace(BF, s4, h4, dq, dkv)
     wsa = torch.empty(max(nba, 256), dtype=torch.uint8, device=dev)
     qkv = 2.0 * s4 * h4 * (dq + 2 * dkv)

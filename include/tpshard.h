@@ -177,6 +177,42 @@ int tp_attn_core_fwd(int dt, int64_t s, int64_t nq, int64_t nkv, int64_t d,
                      void *stream);
 
 /* ------------------------------------------------------------------------ */
+/* Sequence-parallel region ([book] §7.3.6)                                   */
+/* ------------------------------------------------------------------------ */
+
+/* Between a sublayer's reduce-scatter and the next sublayer's all-gather a
+ * card holds only its n = s/t positions; LayerNorm and dropout act on each
+ * position independently.  For every row r of the shard's [n, h] slice:
+ *     u[r] = x[r] + y[r] * mask[r] / (1 - p)            (residual + dropout)
+ *     z[r] = (u[r] - mean[r]) * rstd[r] * gamma + beta   (LayerNorm)
+ * with mean[r] = mean_c u[r][c], rstd[r] = 1 / sqrt(mean_c (u - mean)^2 + eps).
+ * y: the sublayer output after the reduce-scatter; x: the residual stream;
+ * mask [n, h] uint8 (1 keep, 0 drop): the dropout draws, made by the caller
+ * for drop probability p in [0, 1).  u, z [n, h] and gamma, beta [h] in bf16
+ * (dt must be TP_DT_BF16); mean, rstd [n] fp32, kept for the backward.
+ * h <= 16384 (TP_EUNSUPPORTED beyond). */
+int tp_sp_ln_fwd(int dt, int64_t n, int64_t h, float p, float eps,
+                 const void *y, const void *x, const uint8_t *mask,
+                 const void *gamma, const void *beta,
+                 void *u, void *z, float *mean, float *rstd, void *stream);
+
+/* Backward: dz [n, h] is the gradient of z, dun [n, h] the gradient reaching u
+ * along the residual stream from above.  With xh = (u - mean) * rstd and
+ * g = dz * gamma:
+ *     dx = dun + rstd * (g - mean_c g - xh * mean_c(g * xh))   (= du)
+ *     dy = dx * mask / (1 - p)
+ *     dgamma = sum_r dz * xh,  dbeta = sum_r dz    (this slice's share; the
+ *     shards' shares are summed across cards)
+ * ws: scratch of tp_sp_ln_bwd_workspace(dt, n, h) bytes, 256-byte aligned
+ * (per-workgroup partial column sums, reduced in a fixed order). */
+size_t tp_sp_ln_bwd_workspace(int dt, int64_t n, int64_t h);
+int tp_sp_ln_bwd(int dt, int64_t n, int64_t h, float p,
+                 const void *dz, const void *dun, const void *u,
+                 const float *mean, const float *rstd, const void *gamma, const uint8_t *mask,
+                 void *dx, void *dy, void *dgamma, void *dbeta,
+                 void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ */
 /* Vocab-parallel output layer, cross entropy and embedding                   */
 /* ([book] §7.3.4; [lec16] §5.5)                                              */
 /* ------------------------------------------------------------------------ */

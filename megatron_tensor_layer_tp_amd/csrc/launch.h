@@ -50,3 +50,13 @@ hipError_t tp_launch_vocab_embed(int elem_bytes, int64_t n, int64_t Vs, int64_t 
 // causal attention core, head dim 128, bf16 Q [s][nq*128], K/V [s][nkv*128], O like Q, lse [nq][s]
 hipError_t tp_launch_attn_fwd(int64_t s, int64_t nq, int64_t nkv, const void *Q, const void *K, const void *V,
                               void *O, float *lse, hipStream_t st);
+
+// sequence-parallel region (residual + dropout + LayerNorm) on [n, h] bf16 rows
+int tp_sp_ln_passes(int64_t h);        // register passes per row (h <= 8192: 1)
+int tp_sp_ln_bwd_grid(int64_t n);      // workgroups of the backward = partial sums of dgamma/dbeta
+hipError_t tp_launch_sp_ln_fwd(int64_t n, int64_t h, float keep, float eps, const void *y, const void *x,
+                               const uint8_t *mask, const void *gamma, const void *beta, void *u, void *z,
+                               float *mean, float *rstd, hipStream_t st);
+hipError_t tp_launch_sp_ln_bwd(int64_t n, int64_t h, float keep, const void *dz, const void *dun, const void *u,
+                               const float *mean, const float *rstd, const void *gamma, const uint8_t *mask,
+                               void *dx, void *dy, void *dgamma, void *dbeta, float *part, hipStream_t st);

@@ -1,0 +1,336 @@
+// sp.hip -- the sequence-parallel region of a layer on one shard's positions:
+// residual add with dropout, then LayerNorm, and the backward of both
+// ("7.3 模型并行与张量并行" §7.3.6: LayerNorm and dropout act on each position
+// independently, so between a sublayer's reduce-scatter and the next sublayer's
+// all-gather each card keeps only its s/t positions).
+//
+//   forward   u = x + y * mask / (1 - p),  z = (u - mean) * rstd * gamma + beta
+//   backward  du = dun + rstd * (g - mean(g) - xh * mean(g * xh)),  g = dz * gamma,
+//             dx = du,  dy = du * mask / (1 - p),
+//             dgamma = sum_rows dz * xh,  dbeta = sum_rows dz
+//
+// HBM-streaming kernels.  One 256-thread workgroup per row: every element of
+// the row is loaded once into registers (16-byte loads of 8 bf16 when h is a
+// multiple of 8), the row statistics are exact two-pass sums over those
+// registers (wave shuffles, then LDS across the 4 waves), and every output is
+// written once.  The backward's dgamma / dbeta are per-workgroup partial column
+// sums (fixed row order per workgroup) reduced in a second, fixed-order pass.
+#include "launch.h"
+
+namespace {
+
+constexpr int SP_THREADS = 256;
+constexpr int SP_VPT = 4;  // 8-element vectors per thread and pass (a pass covers 8192 columns)
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+__device__ __forceinline__ uint16_t f2bf(float f) {  // round to nearest even
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+__device__ __forceinline__ void unpack8(const u32x4 &w, float *v) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    v[2 * q] = __uint_as_float(w[q] << 16);
+    v[2 * q + 1] = __uint_as_float(w[q] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ u32x4 pack8(const float *v) {
+  u32x4 o;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const f32x2_t p = {v[2 * q], v[2 * q + 1]};
+    o[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2_t));
+  }
+  return o;
+}
+
+// sum over the workgroup (every thread gets the total); `red` holds 4 floats
+__device__ __forceinline__ float block_sum(float v, float *red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// column c of vector slot i of this thread: element 8 * (tid + 256 i) + q
+template <bool VEC>
+__device__ __forceinline__ int col_of(int i, int q) {
+  return VEC ? 8 * ((int)threadIdx.x + SP_THREADS * i) + q : (int)threadIdx.x + SP_THREADS * (8 * i + q);
+}
+
+// load 8 elements (VEC: one 16-byte vector; else strided scalars, 0 past the row end)
+template <bool VEC>
+__device__ __forceinline__ void load8(const uint16_t *row, int i, int h, float *v) {
+  if constexpr (VEC) {
+    const int c = col_of<true>(i, 0);
+    if (c < h) unpack8(*(const u32x4 *)(row + c), v);
+    else
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = 0.f;
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int c = col_of<false>(i, q);
+      v[q] = c < h ? bf2f(row[c]) : 0.f;
+    }
+  }
+}
+template <bool VEC>
+__device__ __forceinline__ void mask8(const uint8_t *row, int i, int h, float *v) {
+  if constexpr (VEC) {
+    const int c = col_of<true>(i, 0);
+    if (c < h) {
+      const uint2 m = *(const uint2 *)(row + c);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = (float)((m.x >> (8 * q)) & 0xffu);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[4 + q] = (float)((m.y >> (8 * q)) & 0xffu);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int c = col_of<false>(i, q);
+      v[q] = c < h ? (float)row[c] : 0.f;
+    }
+  }
+}
+template <bool VEC>
+__device__ __forceinline__ void store8(uint16_t *row, int i, int h, const float *v) {
+  if constexpr (VEC) {
+    const int c = col_of<true>(i, 0);
+    if (c < h) *(u32x4 *)(row + c) = pack8(v);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int c = col_of<false>(i, q);
+      if (c < h) row[c] = f2bf(v[q]);
+    }
+  }
+}
+
+struct SpArgs {
+  int64_t n, h;
+  float keep, eps;  // 1 / (1 - p), LayerNorm epsilon
+  const uint16_t *y, *x, *gamma, *beta, *dz, *dun, *u;
+  const uint8_t *mask;
+  uint16_t *uo, *z, *dx, *dy, *dgamma, *dbeta;
+  float *mean, *rstd, *part;  // part: [grid][2][h] partial column sums
+};
+
+// rows of up to SP_VPT * 8 * 256 = 8192 columns in registers (NP passes for longer rows)
+template <bool VEC, int NP>
+__global__ void __launch_bounds__(SP_THREADS) sp_ln_fwd_kernel(SpArgs a) {
+  __shared__ float red[4];
+  const int h = (int)a.h;
+  for (int64_t r = blockIdx.x; r < a.n; r += gridDim.x) {
+    const uint16_t *yr = a.y + r * a.h, *xr = a.x + r * a.h;
+    const uint8_t *mr = a.mask + r * a.h;
+    float u[NP * SP_VPT][8];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NP * SP_VPT; ++i) {
+      float yv[8], xv[8], mv[8];
+      load8<VEC>(yr, i, h, yv);
+      load8<VEC>(xr, i, h, xv);
+      mask8<VEC>(mr, i, h, mv);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        u[i][q] = fmaf(yv[q] * mv[q], a.keep, xv[q]);
+        s += u[i][q];
+      }
+    }
+    const float mean = block_sum(s, red) / (float)h;
+    float v2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < NP * SP_VPT; ++i)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const bool in = col_of<VEC>(i, q) < h;
+        const float d = u[i][q] - mean;
+        v2 += in ? d * d : 0.f;
+      }
+    const float var = block_sum(v2, red) / (float)h;
+    const float rstd = 1.f / sqrtf(var + a.eps);
+    uint16_t *ur = a.uo + r * a.h, *zr = a.z + r * a.h;
+#pragma unroll
+    for (int i = 0; i < NP * SP_VPT; ++i) {
+      float gv[8], bv[8], zv[8];
+      load8<VEC>(a.gamma, i, h, gv);
+      load8<VEC>(a.beta, i, h, bv);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) zv[q] = fmaf((u[i][q] - mean) * rstd, gv[q], bv[q]);
+      store8<VEC>(ur, i, h, u[i]);
+      store8<VEC>(zr, i, h, zv);
+    }
+    if (threadIdx.x == 0) {
+      a.mean[r] = mean;
+      a.rstd[r] = rstd;
+    }
+  }
+}
+
+template <bool VEC, int NP>
+__global__ void __launch_bounds__(SP_THREADS) sp_ln_bwd_kernel(SpArgs a) {
+  __shared__ float red[4];
+  const int h = (int)a.h;
+  float pg[NP * SP_VPT][8], pb[NP * SP_VPT][8];  // this workgroup's partial dgamma, dbeta
+#pragma unroll
+  for (int i = 0; i < NP * SP_VPT; ++i)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) pg[i][q] = pb[i][q] = 0.f;
+  float gam[NP * SP_VPT][8];
+#pragma unroll
+  for (int i = 0; i < NP * SP_VPT; ++i) load8<VEC>(a.gamma, i, h, gam[i]);
+  for (int64_t r = blockIdx.x; r < a.n; r += gridDim.x) {
+    const float mean = a.mean[r], rstd = a.rstd[r];
+    float xh[NP * SP_VPT][8], g[NP * SP_VPT][8];
+    float sg = 0.f, sgx = 0.f;
+#pragma unroll
+    for (int i = 0; i < NP * SP_VPT; ++i) {
+      float uv[8], dzv[8];
+      load8<VEC>(a.u + r * a.h, i, h, uv);
+      load8<VEC>(a.dz + r * a.h, i, h, dzv);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const bool in = col_of<VEC>(i, q) < h;
+        xh[i][q] = in ? (uv[q] - mean) * rstd : 0.f;
+        g[i][q] = dzv[q] * gam[i][q];
+        sg += g[i][q];
+        sgx += g[i][q] * xh[i][q];
+        pg[i][q] = fmaf(dzv[q], xh[i][q], pg[i][q]);
+        pb[i][q] += dzv[q];
+      }
+    }
+    const float mg = block_sum(sg, red) / (float)h;
+    const float mgx = block_sum(sgx, red) / (float)h;
+#pragma unroll
+    for (int i = 0; i < NP * SP_VPT; ++i) {
+      float dn[8], mv[8], dxv[8], dyv[8];
+      load8<VEC>(a.dun + r * a.h, i, h, dn);
+      mask8<VEC>(a.mask + r * a.h, i, h, mv);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        dxv[q] = fmaf(rstd, g[i][q] - mg - xh[i][q] * mgx, dn[q]);
+        dyv[q] = dxv[q] * mv[q] * a.keep;
+      }
+      store8<VEC>(a.dx + r * a.h, i, h, dxv);
+      store8<VEC>(a.dy + r * a.h, i, h, dyv);
+    }
+  }
+  float *pr = a.part + (int64_t)blockIdx.x * 2 * a.h;
+#pragma unroll
+  for (int i = 0; i < NP * SP_VPT; ++i)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int c = col_of<VEC>(i, q);
+      if (c < h) {
+        pr[c] = pg[i][q];
+        pr[a.h + c] = pb[i][q];
+      }
+    }
+}
+
+// dgamma[c], dbeta[c] = sum over the partials in workgroup order
+__global__ void __launch_bounds__(256) sp_ln_param_reduce_kernel(const float *__restrict__ part, int nparts,
+                                                                 int64_t h, uint16_t *__restrict__ dgamma,
+                                                                 uint16_t *__restrict__ dbeta) {
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < h; c += (int64_t)gridDim.x * blockDim.x) {
+    float sg = 0.f, sb = 0.f;
+    for (int k = 0; k < nparts; ++k) {
+      sg += part[(int64_t)k * 2 * h + c];
+      sb += part[(int64_t)k * 2 * h + h + c];
+    }
+    dgamma[c] = f2bf(sg);
+    dbeta[c] = f2bf(sb);
+  }
+}
+
+template <int NP>
+hipError_t launch_fwd(const SpArgs &a, bool vec, hipStream_t st) {
+  const unsigned grid = (unsigned)(a.n < 1048576 ? a.n : 1048576);
+  if (vec) hipLaunchKernelGGL((sp_ln_fwd_kernel<true, NP>), dim3(grid), dim3(SP_THREADS), 0, st, a);
+  else hipLaunchKernelGGL((sp_ln_fwd_kernel<false, NP>), dim3(grid), dim3(SP_THREADS), 0, st, a);
+  return hipGetLastError();
+}
+template <int NP>
+hipError_t launch_bwd(const SpArgs &a, bool vec, int grid, hipStream_t st) {
+  if (vec) hipLaunchKernelGGL((sp_ln_bwd_kernel<true, NP>), dim3(grid), dim3(SP_THREADS), 0, st, a);
+  else hipLaunchKernelGGL((sp_ln_bwd_kernel<false, NP>), dim3(grid), dim3(SP_THREADS), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int tp_sp_ln_passes(int64_t h) { return (int)((h + SP_VPT * 8 * SP_THREADS - 1) / (SP_VPT * 8 * SP_THREADS)); }
+
+int tp_sp_ln_bwd_grid(int64_t n) { return (int)(n < 256 ? (n > 0 ? n : 1) : 256); }
+
+hipError_t tp_launch_sp_ln_fwd(int64_t n, int64_t h, float keep, float eps, const void *y, const void *x,
+                               const uint8_t *mask, const void *gamma, const void *beta, void *u, void *z,
+                               float *mean, float *rstd, hipStream_t st) {
+  if (n == 0 || h == 0) return hipSuccess;
+  SpArgs a = {};
+  a.n = n;
+  a.h = h;
+  a.keep = keep;
+  a.eps = eps;
+  a.y = (const uint16_t *)y;
+  a.x = (const uint16_t *)x;
+  a.mask = mask;
+  a.gamma = (const uint16_t *)gamma;
+  a.beta = (const uint16_t *)beta;
+  a.uo = (uint16_t *)u;
+  a.z = (uint16_t *)z;
+  a.mean = mean;
+  a.rstd = rstd;
+  const bool vec = h % 8 == 0;
+  switch (tp_sp_ln_passes(h)) {
+  case 1: return launch_fwd<1>(a, vec, st);
+  case 2: return launch_fwd<2>(a, vec, st);
+  default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t tp_launch_sp_ln_bwd(int64_t n, int64_t h, float keep, const void *dz, const void *dun, const void *u,
+                               const float *mean, const float *rstd, const void *gamma, const uint8_t *mask,
+                               void *dx, void *dy, void *dgamma, void *dbeta, float *part, hipStream_t st) {
+  if (h == 0) return hipSuccess;
+  SpArgs a = {};
+  a.n = n;
+  a.h = h;
+  a.keep = keep;
+  a.dz = (const uint16_t *)dz;
+  a.dun = (const uint16_t *)dun;
+  a.u = (const uint16_t *)u;
+  a.mean = const_cast<float *>(mean);
+  a.rstd = const_cast<float *>(rstd);
+  a.gamma = (const uint16_t *)gamma;
+  a.mask = mask;
+  a.dx = (uint16_t *)dx;
+  a.dy = (uint16_t *)dy;
+  a.part = part;
+  const bool vec = h % 8 == 0;
+  const int grid = tp_sp_ln_bwd_grid(n);
+  hipError_t e;
+  switch (tp_sp_ln_passes(h)) {
+  case 1: e = launch_bwd<1>(a, vec, grid, st); break;
+  case 2: e = launch_bwd<2>(a, vec, grid, st); break;
+  default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  const int64_t rb = (h + 255) / 256;
+  hipLaunchKernelGGL(sp_ln_param_reduce_kernel, dim3((unsigned)(rb < 65536 ? rb : 65536)), dim3(256), 0, st, part,
+                     grid, h, (uint16_t *)dgamma, (uint16_t *)dbeta);
+  return hipGetLastError();
+}

@@ -920,6 +920,57 @@ int tp_attn_core_fwd(int dt, int64_t s, int64_t nq, int64_t nkv, int64_t d, cons
   return ok();
 }
 
+int tp_sp_ln_fwd(int dt, int64_t n, int64_t h, float p, float eps, const void *y, const void *x,
+                 const uint8_t *mask, const void *gamma, const void *beta, void *u, void *z, float *mean,
+                 float *rstd, void *stream) {
+  Checker c;
+  int64_t ne;
+  c.dtype(dt, false, "tp_sp_ln_fwd");
+  c.dim(n, "n") && c.dim(h, "h");
+  if (!c.status && !(p >= 0.f && p < 1.f)) c.status = fail(TP_EINVAL, "tp_sp_ln_fwd: dropout p = %g not in [0, 1)", p);
+  if (!c.status && !(eps > 0.f)) c.status = fail(TP_EINVAL, "tp_sp_ln_fwd: eps = %g is not positive", eps);
+  if (!c.status && tp_sp_ln_passes(h) > 2) c.status = fail(TP_EUNSUPPORTED, "tp_sp_ln_fwd: h = %lld > 16384", (long long)h);
+  c.elems(n, h, ne, "x");
+  c.ptr(y, ne, "y") && c.ptr(x, ne, "x") && c.ptr(mask, ne, "mask") && c.ptr(gamma, h, "gamma") &&
+      c.ptr(beta, h, "beta") && c.ptr(u, ne, "u") && c.ptr(z, ne, "z") && c.ptr(mean, n, "mean") &&
+      c.ptr(rstd, n, "rstd");
+  if (c.status) return c.status;
+  hipError_t e = tp_launch_sp_ln_fwd(n, h, 1.f / (1.f - p), eps, y, x, mask, gamma, beta, u, z, mean, rstd,
+                                     (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TP_EHIP, "tp_sp_ln_fwd: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t tp_sp_ln_bwd_workspace(int dt, int64_t n, int64_t h) {
+  Checker c;
+  c.dtype(dt, false, "tp_sp_ln_bwd_workspace");
+  c.dim(n, "n") && c.dim(h, "h");
+  if (c.status) return 0;
+  return align256((size_t)tp_sp_ln_bwd_grid(n) * 2 * h * sizeof(float));
+}
+
+int tp_sp_ln_bwd(int dt, int64_t n, int64_t h, float p, const void *dz, const void *dun, const void *u,
+                 const float *mean, const float *rstd, const void *gamma, const uint8_t *mask, void *dx, void *dy,
+                 void *dgamma, void *dbeta, void *ws, size_t ws_bytes, void *stream) {
+  Checker c;
+  int64_t ne;
+  c.dtype(dt, false, "tp_sp_ln_bwd");
+  c.dim(n, "n") && c.dim(h, "h");
+  if (!c.status && !(p >= 0.f && p < 1.f)) c.status = fail(TP_EINVAL, "tp_sp_ln_bwd: dropout p = %g not in [0, 1)", p);
+  if (!c.status && tp_sp_ln_passes(h) > 2) c.status = fail(TP_EUNSUPPORTED, "tp_sp_ln_bwd: h = %lld > 16384", (long long)h);
+  c.elems(n, h, ne, "dz");
+  c.ptr(dz, ne, "dz") && c.ptr(dun, ne, "dun") && c.ptr(u, ne, "u") && c.ptr(mean, n, "mean") &&
+      c.ptr(rstd, n, "rstd") && c.ptr(gamma, h, "gamma") && c.ptr(mask, ne, "mask") && c.ptr(dx, ne, "dx") &&
+      c.ptr(dy, ne, "dy") && c.ptr(dgamma, h, "dgamma") && c.ptr(dbeta, h, "dbeta");
+  if (c.status) return c.status;
+  ws_ok(c, ws, ws_bytes, h ? align256((size_t)tp_sp_ln_bwd_grid(n) * 2 * h * sizeof(float)) : 0, "tp_sp_ln_bwd");
+  if (c.status) return c.status;
+  hipError_t e = tp_launch_sp_ln_bwd(n, h, 1.f / (1.f - p), dz, dun, u, mean, rstd, gamma, mask, dx, dy, dgamma,
+                                     dbeta, (float *)ws, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TP_EHIP, "tp_sp_ln_bwd: %s", hipGetErrorString(e));
+  return ok();
+}
+
 size_t tp_lm_head_ce_workspace(int dt, int64_t s, int64_t h, int64_t Vs) {
   Checker c;
   c.dtype(dt, false, "tp_lm_head_ce_workspace");

@@ -27,6 +27,7 @@ ENTROPY = 20261202
 T_X, T_W1, T_W2, T_DY, T_WG, T_WU, T_WD, T_WQ, T_WK, T_WV, T_WO, T_O, T_DQ, T_DK, \
     T_DV, T_HF, T_WLM, T_TGT, T_TABLE, T_IDS, T_LOGITS = range(21)
 T_AQ, T_AK, T_AV = 21, 22, 23   # attention-core inputs
+T_SPY, T_SPX, T_SPMASK, T_SPG, T_SPB, T_SPDZ, T_SPDUN = range(24, 31)   # sequence-parallel region
 
 
 def _rng(config: int, tensor: int, shard: int = 0) -> np.random.Generator:
@@ -201,6 +202,24 @@ def attn_core_inputs(cfg_id: int = 4, shards=(0,), s=None):
     for name, tid, w in (("Q", T_AQ, dq), ("K", T_AK, dkv), ("V", T_AV, dkv)):
         out[name] = {i: normal_bf16((s, w), 1.0, cfg_id, tid, i) for i in shards}
     return out
+
+
+def sp_inputs(cfg_id: int = 4, n=None, h=None, p: float = 0.1):
+    """Sequence-parallel region inputs for one shard's n = s/t positions (bf16
+    bits unless stated): y (sublayer output after the reduce-scatter) and x
+    (residual stream) N(0,1); a dropout mask [n,h] uint8 with P(keep) = 1 - p;
+    LayerNorm gamma ~ 1 + N(0, 0.1^2), beta ~ N(0, 0.1^2); and the backward's
+    dz, dun ~ N(0,1)."""
+    c = CONFIGS[cfg_id]
+    n = c["s"] // c["t"] if n is None else n
+    h = c["h"] if h is None else h
+    keep = _rng(cfg_id, T_SPMASK).random((n, h)) >= p
+    g = _rng(cfg_id, T_SPG).standard_normal(h).astype(np.float32)
+    return {"n": n, "h": h, "p": p,
+            "y": normal_bf16((n, h), 1.0, cfg_id, T_SPY), "x": normal_bf16((n, h), 1.0, cfg_id, T_SPX),
+            "mask": keep.astype(np.uint8),
+            "gamma": f32_to_bf16_bits(1.0 + 0.1 * g), "beta": normal_bf16((h,), 0.1, cfg_id, T_SPB),
+            "dz": normal_bf16((n, h), 1.0, cfg_id, T_SPDZ), "dun": normal_bf16((n, h), 1.0, cfg_id, T_SPDUN)}
 
 
 def vocab_inputs(cfg_id: int = 5, shards=(0,), s=None, h=None, V=None, t=None,

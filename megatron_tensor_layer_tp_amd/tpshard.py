@@ -38,6 +38,9 @@ _SIGS = {
     "tp_vocab_ce": (_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
     "tp_vocab_ce_bwd": (_int, [_int, _i64, _i64, _i64] + [_vp] * 6 + [_vp]),
     "tp_attn_core_fwd": (_int, [_int, _i64, _i64, _i64, _i64] + [_vp] * 5 + [_vp]),
+    "tp_sp_ln_fwd": (_int, [_int, _i64, _i64, ctypes.c_float, ctypes.c_float] + [_vp] * 9 + [_vp]),
+    "tp_sp_ln_bwd_workspace": (_sz, [_int, _i64, _i64]),
+    "tp_sp_ln_bwd": (_int, [_int, _i64, _i64, ctypes.c_float] + [_vp] * 11 + [_vp, _sz, _vp]),
     "tp_lm_head_ce_workspace": (_sz, [_int, _i64, _i64, _i64]),
     "tp_lm_head_ce_fwd": (_int, [_int, _i64, _i64, _i64, _i64] + [_vp] * 6 + [_vp, _sz, _vp]),
     "tp_vocab_embed": (_int, [_int, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
@@ -169,6 +172,21 @@ def tp_lm_head_fwd(dt, s, h, Vs, Hf, Wlm, logits, stream=None):
 def tp_attn_core_fwd(dt, s, nq, nkv, d, Q, K, V, O, lse, stream=None):
     return _call("tp_attn_core_fwd", dt, s, nq, nkv, d, _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(lse),
                  _stream(stream))
+
+
+def tp_sp_ln_fwd(dt, n, h, p, eps, y, x, mask, gamma, beta, u, z, mean, rstd, stream=None):
+    return _call("tp_sp_ln_fwd", dt, n, h, p, eps, _ptr(y), _ptr(x), _ptr(mask), _ptr(gamma), _ptr(beta),
+                 _ptr(u), _ptr(z), _ptr(mean), _ptr(rstd), _stream(stream))
+
+
+def tp_sp_ln_bwd_workspace(dt, n, h):
+    return lib().tp_sp_ln_bwd_workspace(dt, n, h)
+
+
+def tp_sp_ln_bwd(dt, n, h, p, dz, dun, u, mean, rstd, gamma, mask, dx, dy, dgamma, dbeta, ws, ws_bytes,
+                 stream=None):
+    return _call("tp_sp_ln_bwd", dt, n, h, p, _ptr(dz), _ptr(dun), _ptr(u), _ptr(mean), _ptr(rstd), _ptr(gamma),
+                 _ptr(mask), _ptr(dx), _ptr(dy), _ptr(dgamma), _ptr(dbeta), _ptr(ws), ws_bytes, _stream(stream))
 
 
 def tp_vocab_ce_bwd(dt, s, Vs, vocab_start, logits, target, gmax, gsum, dloss, dlogits, stream=None):

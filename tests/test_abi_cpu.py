@@ -34,7 +34,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert len(names) == 19, names
+    assert len(names) == 22, names
     raw = ctypes.CDLL(T.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -182,3 +182,27 @@ def test_attn_core_validation(L):
     assert _st(L, "tp_attn_core_fwd", *bad) == T.TP_EALIGN
     # nothing to compute: no positions
     assert _st(L, "tp_attn_core_fwd", T.TP_DT_BF16, 0, 8, 1, 128, None, None, None, None, None, None) == T.TP_OK
+
+
+def test_sp_validation(L):
+    import ctypes as C
+    f = [T.TP_DT_BF16, 16, 64, C.c_float(0.1), C.c_float(1e-5)] + [A16] * 9 + [None]
+    bad = list(f)
+    bad[3] = C.c_float(1.0)
+    assert _st(L, "tp_sp_ln_fwd", *bad) == T.TP_EINVAL
+    bad = list(f)
+    bad[4] = C.c_float(0.0)
+    assert _st(L, "tp_sp_ln_fwd", *bad) == T.TP_EINVAL
+    bad = list(f)
+    bad[2] = 20000
+    assert _st(L, "tp_sp_ln_fwd", *bad) == T.TP_EUNSUPPORTED
+    bad = list(f)
+    bad[7] = None  # mask
+    assert _st(L, "tp_sp_ln_fwd", *bad) == T.TP_EINVAL
+    need = T.tp_sp_ln_bwd_workspace(T.TP_DT_BF16, 1024, 8192)
+    assert need >= 256 * 2 * 8192 * 4
+    b = [T.TP_DT_BF16, 1024, 8192, C.c_float(0.1)] + [A16] * 11
+    assert _st(L, "tp_sp_ln_bwd", *b, A16, need - 1, None) == T.TP_EWORKSPACE
+    assert _st(L, "tp_sp_ln_bwd", *b, A16 + 64, need, None) == T.TP_EALIGN
+    assert _st(L, "tp_sp_ln_fwd", T.TP_DT_BF16, 0, 64, C.c_float(0.1), C.c_float(1e-5), None, None, None, A16, A16,
+               None, None, None, None, None) == T.TP_OK
