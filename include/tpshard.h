@@ -204,7 +204,7 @@ int tp_sp_ln_fwd(int dt, int64_t n, int64_t h, float p, float eps,
  *     dgamma = sum_r dz * xh,  dbeta = sum_r dz    (this slice's share; the
  *     shards' shares are summed across cards)
  * ws: scratch of tp_sp_ln_bwd_workspace(dt, n, h) bytes, 256-byte aligned
- * (per-workgroup partial column sums, reduced in a fixed order). */
+ * (partial column sums of each 16-row chunk, reduced in a fixed order). */
 size_t tp_sp_ln_bwd_workspace(int dt, int64_t n, int64_t h);
 int tp_sp_ln_bwd(int dt, int64_t n, int64_t h, float p,
                  const void *dz, const void *dun, const void *u,

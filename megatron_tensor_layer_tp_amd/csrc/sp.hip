@@ -13,8 +13,9 @@
 // the row is loaded once into registers (16-byte loads of 8 bf16 when h is a
 // multiple of 8), the row statistics are exact two-pass sums over those
 // registers (wave shuffles, then LDS across the 4 waves), and every output is
-// written once.  The backward's dgamma / dbeta are per-workgroup partial column
-// sums (fixed row order per workgroup) reduced in a second, fixed-order pass.
+// written once.  The backward's dgamma / dbeta are column sums over the rows:
+// a second kernel sums chunks of 16 rows per column (16-byte loads across the
+// row) into partials that a third reduces in chunk order (deterministic).
 #include "launch.h"
 
 namespace {
@@ -125,7 +126,7 @@ struct SpArgs {
   const uint16_t *y, *x, *gamma, *beta, *dz, *dun, *u;
   const uint8_t *mask;
   uint16_t *uo, *z, *dx, *dy, *dgamma, *dbeta;
-  float *mean, *rstd, *part;  // part: [grid][2][h] partial column sums
+  float *mean, *rstd, *part;  // part: [row chunks][2][h] partial column sums
 };
 
 // rows of up to SP_VPT * 8 * 256 = 8192 columns in registers (NP passes for longer rows)
@@ -184,32 +185,23 @@ template <bool VEC, int NP>
 __global__ void __launch_bounds__(SP_THREADS) sp_ln_bwd_kernel(SpArgs a) {
   __shared__ float red[4];
   const int h = (int)a.h;
-  float pg[NP * SP_VPT][8], pb[NP * SP_VPT][8];  // this workgroup's partial dgamma, dbeta
-#pragma unroll
-  for (int i = 0; i < NP * SP_VPT; ++i)
-#pragma unroll
-    for (int q = 0; q < 8; ++q) pg[i][q] = pb[i][q] = 0.f;
-  float gam[NP * SP_VPT][8];
-#pragma unroll
-  for (int i = 0; i < NP * SP_VPT; ++i) load8<VEC>(a.gamma, i, h, gam[i]);
   for (int64_t r = blockIdx.x; r < a.n; r += gridDim.x) {
     const float mean = a.mean[r], rstd = a.rstd[r];
     float xh[NP * SP_VPT][8], g[NP * SP_VPT][8];
     float sg = 0.f, sgx = 0.f;
 #pragma unroll
     for (int i = 0; i < NP * SP_VPT; ++i) {
-      float uv[8], dzv[8];
+      float uv[8], dzv[8], gv[8];
       load8<VEC>(a.u + r * a.h, i, h, uv);
       load8<VEC>(a.dz + r * a.h, i, h, dzv);
+      load8<VEC>(a.gamma, i, h, gv);
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const bool in = col_of<VEC>(i, q) < h;
         xh[i][q] = in ? (uv[q] - mean) * rstd : 0.f;
-        g[i][q] = dzv[q] * gam[i][q];
+        g[i][q] = dzv[q] * gv[q];
         sg += g[i][q];
         sgx += g[i][q] * xh[i][q];
-        pg[i][q] = fmaf(dzv[q], xh[i][q], pg[i][q]);
-        pb[i][q] += dzv[q];
       }
     }
     const float mg = block_sum(sg, red) / (float)h;
@@ -228,16 +220,46 @@ __global__ void __launch_bounds__(SP_THREADS) sp_ln_bwd_kernel(SpArgs a) {
       store8<VEC>(a.dy + r * a.h, i, h, dyv);
     }
   }
-  float *pr = a.part + (int64_t)blockIdx.x * 2 * a.h;
+}
+
+// dgamma / dbeta partial column sums over one chunk of SP_RCHUNK rows (rows in
+// increasing order): thread i of the grid's x dimension owns columns 8i .. 8i+7.
+constexpr int SP_RCHUNK = 16;
+__global__ void __launch_bounds__(256) sp_ln_param_partial_kernel(SpArgs a) {
+  const int64_t c0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
+  if (c0 >= a.h) return;
+  const int64_t r0 = (int64_t)blockIdx.y * SP_RCHUNK, r1 = min(a.n, r0 + SP_RCHUNK);
+  float pg[8], pb[8];
 #pragma unroll
-  for (int i = 0; i < NP * SP_VPT; ++i)
+  for (int q = 0; q < 8; ++q) pg[q] = pb[q] = 0.f;
+  const bool full = c0 + 8 <= a.h && (a.h & 7) == 0;
+#pragma unroll 4
+  for (int64_t r = r0; r < r1; ++r) {
+    const float mean = a.mean[r], rstd = a.rstd[r];
+    float uv[8], dzv[8];
+    if (full) {
+      unpack8(*(const u32x4 *)(a.u + r * a.h + c0), uv);
+      unpack8(*(const u32x4 *)(a.dz + r * a.h + c0), dzv);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const bool in = c0 + q < a.h;
+        uv[q] = in ? bf2f(a.u[r * a.h + c0 + q]) : 0.f;
+        dzv[q] = in ? bf2f(a.dz[r * a.h + c0 + q]) : 0.f;
+      }
+    }
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      const int c = col_of<VEC>(i, q);
-      if (c < h) {
-        pr[c] = pg[i][q];
-        pr[a.h + c] = pb[i][q];
-      }
+      pg[q] = fmaf(dzv[q], (uv[q] - mean) * rstd, pg[q]);
+      pb[q] += dzv[q];
+    }
+  }
+  float *pr = a.part + (int64_t)blockIdx.y * 2 * a.h;
+#pragma unroll
+  for (int q = 0; q < 8; ++q)
+    if (c0 + q < a.h) {
+      pr[c0 + q] = pg[q];
+      pr[a.h + c0 + q] = pb[q];
     }
 }
 
@@ -247,6 +269,7 @@ __global__ void __launch_bounds__(256) sp_ln_param_reduce_kernel(const float *__
                                                                  uint16_t *__restrict__ dbeta) {
   for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < h; c += (int64_t)gridDim.x * blockDim.x) {
     float sg = 0.f, sb = 0.f;
+#pragma unroll 16
     for (int k = 0; k < nparts; ++k) {
       sg += part[(int64_t)k * 2 * h + c];
       sb += part[(int64_t)k * 2 * h + h + c];
@@ -264,7 +287,8 @@ hipError_t launch_fwd(const SpArgs &a, bool vec, hipStream_t st) {
   return hipGetLastError();
 }
 template <int NP>
-hipError_t launch_bwd(const SpArgs &a, bool vec, int grid, hipStream_t st) {
+hipError_t launch_bwd(const SpArgs &a, bool vec, hipStream_t st) {
+  const unsigned grid = (unsigned)(a.n < 1048576 ? a.n : 1048576);
   if (vec) hipLaunchKernelGGL((sp_ln_bwd_kernel<true, NP>), dim3(grid), dim3(SP_THREADS), 0, st, a);
   else hipLaunchKernelGGL((sp_ln_bwd_kernel<false, NP>), dim3(grid), dim3(SP_THREADS), 0, st, a);
   return hipGetLastError();
@@ -274,7 +298,10 @@ hipError_t launch_bwd(const SpArgs &a, bool vec, int grid, hipStream_t st) {
 
 int tp_sp_ln_passes(int64_t h) { return (int)((h + SP_VPT * 8 * SP_THREADS - 1) / (SP_VPT * 8 * SP_THREADS)); }
 
-int tp_sp_ln_bwd_grid(int64_t n) { return (int)(n < 256 ? (n > 0 ? n : 1) : 256); }
+int tp_sp_ln_bwd_grid(int64_t n) {
+  const int64_t chunks = (n + SP_RCHUNK - 1) / SP_RCHUNK;
+  return (int)(chunks > 0 ? chunks : 1);
+}
 
 hipError_t tp_launch_sp_ln_fwd(int64_t n, int64_t h, float keep, float eps, const void *y, const void *x,
                                const uint8_t *mask, const void *gamma, const void *beta, void *u, void *z,
@@ -321,16 +348,21 @@ hipError_t tp_launch_sp_ln_bwd(int64_t n, int64_t h, float keep, const void *dz,
   a.dy = (uint16_t *)dy;
   a.part = part;
   const bool vec = h % 8 == 0;
-  const int grid = tp_sp_ln_bwd_grid(n);
-  hipError_t e;
-  switch (tp_sp_ln_passes(h)) {
-  case 1: e = launch_bwd<1>(a, vec, grid, st); break;
-  case 2: e = launch_bwd<2>(a, vec, grid, st); break;
-  default: return hipErrorInvalidValue;
+  const int chunks = tp_sp_ln_bwd_grid(n);
+  hipError_t e = hipSuccess;
+  if (n > 0) {
+    switch (tp_sp_ln_passes(h)) {
+    case 1: e = launch_bwd<1>(a, vec, st); break;
+    case 2: e = launch_bwd<2>(a, vec, st); break;
+    default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
   }
-  if (e != hipSuccess) return e;
+  const int64_t cb = (h + 8 * 256 - 1) / (8 * 256);
+  hipLaunchKernelGGL(sp_ln_param_partial_kernel, dim3((unsigned)cb, (unsigned)chunks), dim3(256), 0, st, a);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   const int64_t rb = (h + 255) / 256;
   hipLaunchKernelGGL(sp_ln_param_reduce_kernel, dim3((unsigned)(rb < 65536 ? rb : 65536)), dim3(256), 0, st, part,
-                     grid, h, (uint16_t *)dgamma, (uint16_t *)dbeta);
+                     chunks, h, (uint16_t *)dgamma, (uint16_t *)dbeta);
   return hipGetLastError();
 }
