@@ -92,34 +92,48 @@ class Row:
 
 
 class GpuSampler:
-    """Best-effort shader clock and temperature of the GPU during the timed
-    steps, read from the amdgpu hwmon files in sysfs (read-only); empty when
-    the files are not there."""
+    """Best-effort shader clock, power and temperatures of the GPU during the
+    timed steps, read (read-only) from the amdgpu sysfs files: the current
+    level of pp_dpm_sclk and the hwmon power and temperature inputs.  Empty
+    when the files are not there."""
 
     def __init__(self):
         import glob
         import threading
         self.files = {}
-        for hw in sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*")):
-            f = os.path.join(hw, "freq1_input")
-            if os.path.exists(f):
-                self.files["sclk_mhz"] = (f, 1e-6)
+        for dev in sorted(glob.glob("/sys/class/drm/*/device")):
+            if not os.path.exists(os.path.join(dev, "pp_dpm_sclk")):
+                continue
+            self.files["sclk_mhz"] = (os.path.join(dev, "pp_dpm_sclk"), None)
+            for hw in sorted(glob.glob(os.path.join(dev, "hwmon", "hwmon*"))):
+                if os.path.exists(os.path.join(hw, "power1_input")):
+                    self.files["power_w"] = (os.path.join(hw, "power1_input"), 1e-6)
                 for t in sorted(glob.glob(os.path.join(hw, "temp*_input"))):
                     lab = t.replace("_input", "_label")
                     name = open(lab).read().strip() if os.path.exists(lab) else os.path.basename(t)[:-6]
                     self.files[f"temp_{name}_c"] = (t, 1e-3)
-                break
+            break
         self.samples = {k: [] for k in self.files}
         self._stop = threading.Event()
         self._thread = threading.Thread(target=self._run, daemon=True)
+
+    @staticmethod
+    def _read(f, scale):
+        with open(f) as fh:
+            txt = fh.read()
+        if scale is not None:
+            return float(txt) * scale
+        for line in txt.splitlines():  # "1: 2100Mhz *" marks the current level
+            if line.strip().endswith("*"):
+                return float(line.split(":")[1].strip().split("M")[0])
+        raise ValueError("no current level")
 
     def _run(self):
         while not self._stop.is_set():
             for k, (f, scale) in self.files.items():
                 try:
-                    with open(f) as fh:
-                        self.samples[k].append(float(fh.read()) * scale)
-                except (OSError, ValueError):
+                    self.samples[k].append(self._read(f, scale))
+                except (OSError, ValueError, IndexError):
                     pass
             self._stop.wait(0.01)
 
