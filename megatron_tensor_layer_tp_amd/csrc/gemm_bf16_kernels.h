@@ -380,10 +380,10 @@ __device__ __forceinline__ void ce_stats8(const GemmDesc &d, int gm, int gn, int
 // column l%32 of the block.  `ep` is this wave's private strip (32 x (WTN+8)).
 // All waves of the workgroup must call it (it holds workgroup barriers).
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int EPI, bool OUT_F32, bool VEC, bool DUAL>
-__device__ __forceinline__ void epilogue(const GemmDesc &d, f32x16 (&acc)[BM / 64][BN / 64], float *ep, int lane,
-                                         int wm, int wn, int m0, int n0, int nlen, int sc, int split) {
-  constexpr int WTM = BM / 2, WTN = BN / 2, FM = WTM / 32, FN = WTN / 32;
+template <int BM, int BN, int EPI, bool OUT_F32, bool VEC, bool DUAL, int NW = 4>
+__device__ __forceinline__ void epilogue(const GemmDesc &d, f32x16 (&acc)[BM / 64][2 * BN / NW / 32], float *ep,
+                                         int lane, int wm, int wn, int m0, int n0, int nlen, int sc, int split) {
+  constexpr int WTM = BM / 2, WTN = BN / (NW / 2), FM = WTM / 32, FN = WTN / 32;
   constexpr int EPS = WTN + 8;                      // strip row stride (floats)
   constexpr int OUTW = DUAL ? WTN / 2 : WTN;        // output columns per strip row
   constexpr int LPR = OUTW / 8;                     // lanes per strip row
@@ -643,11 +643,12 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // One operand tile (R rows of 64 k, or 64 k-rows of R columns) staged by
-// R/32 one-kilobyte DMA instructions per wave.  DUAL: the R columns are two
+// R/(8 NW) one-kilobyte DMA instructions per wave (NW waves).  DUAL: the R columns are two
 // sub-tiles of R/2 from two matrices; waves 0-1 fill the first, 2-3 the second.
-template <int R, bool KC, bool DUAL>
+template <int R, bool KC, bool DUAL, int NW = 4>
 struct Dma {
-  static constexpr int NI = R / 32;
+  static_assert(!DUAL || NW == 4, "the dual operand is staged by 4 waves");
+  static constexpr int NI = R / (8 * NW);  // kilobytes per wave
   static constexpr int REFF = DUAL ? R / 2 : R;   // columns of one row-contiguous sub-tile
   static constexpr int P = 2 * REFF;              // its k-row pitch (bytes)
   uint32_t vo[NI];   // per-lane byte offset within the block
@@ -725,14 +726,18 @@ __device__ __forceinline__ bf16x8 read_tr(const char *p0, const char *p1) {
 // The whole tile computation of the DMA kernel for logical tile id `lid`;
 // smem0 / smem1 are the two LDS stages (each at least 128 * (BM + BN) bytes)
 // declared by the calling kernel.
-template <int BM, int BN, bool A_KC, bool B_KC, int EPI, bool OUT_F32, bool KSEG>
-__device__ __forceinline__ void dma_body(const GemmDesc &d, int lid, char *smem0, char *smem1) {
+template <int BM, int BN, bool A_KC, bool B_KC, int EPI, bool OUT_F32, bool KSEG, int NW = 4, int NS = 2>
+__device__ __forceinline__ void dma_body(const GemmDesc &d, int lid, char *smem0, char *smem1,
+                                         char *smem2 = nullptr) {
+  static_assert(NS == 2 || NS == 3, "two or three LDS stages");
   constexpr bool DUAL = EPI == EPI_SWIGLU_FWD;
   static_assert(!(DUAL && (B_KC || KSEG)), "the dual gate/up operand is an n-contiguous weight");
-  constexpr int WTM = BM / 2, WTN = BN / 2, FM = WTM / 32, FN = WTN / 32;
+  // NW waves in a 2 x NW/2 grid, each a (BM/2) x (BN/(NW/2)) sub-tile
+  constexpr int WGN = NW / 2;
+  constexpr int WTM = BM / 2, WTN = BN / WGN, FM = WTM / 32, FN = WTN / 32;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wid >> 1, wn = wid & 1;
+  const int wm = wid / WGN, wn = wid % WGN;
 
   int tm, tn, split;
   tile_of(d, lid, tm, tn, split);
@@ -747,8 +752,8 @@ __device__ __forceinline__ void dma_body(const GemmDesc &d, int lid, char *smem0
   const int kt_begin = split * d.kt_per_split;
   const int kt_end = min(kt_total, kt_begin + d.kt_per_split);
 
-  using DA = Dma<BM, A_KC, false>;
-  using DB = Dma<BN, B_KC, DUAL>;
+  using DA = Dma<BM, A_KC, false, NW>;
+  using DB = Dma<BN, B_KC, DUAL, NW>;
   constexpr int NLD = DA::NI + DB::NI;  // DMA instructions per wave per tile
   DA da;
   DB db;
@@ -881,40 +886,70 @@ __device__ __forceinline__ void dma_body(const GemmDesc &d, int lid, char *smem0
   const uint32_t L0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(smem0));
   const uint32_t L1 = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(smem1));
   const int nk = kt_end - kt_begin;
-  if (nk > 0) {
-    prep();
+  if constexpr (NS == 2) {
+    if (nk > 0) {
+      prep();
 #pragma unroll
-    for (int q = 0; q < NLD; ++q) dma_q(q, L0);
-  }
-  for (int t = 0; t < nk; ++t) {
-    const char *cur = (t & 1) ? smem1 : smem0;
-    const uint32_t nxt = (t & 1) ? L0 : L1;
-    // this wave's DMA of tile t is the only DMA outstanding here
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    lds_barrier();
-    step(cur, nxt, t + 1 < nk);
+      for (int q = 0; q < NLD; ++q) dma_q(q, L0);
+    }
+    for (int t = 0; t < nk; ++t) {
+      const char *cur = (t & 1) ? smem1 : smem0;
+      const uint32_t nxt = (t & 1) ? L0 : L1;
+      // this wave's DMA of tile t is the only DMA outstanding here
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      lds_barrier();
+      step(cur, nxt, t + 1 < nk);
+    }
+  } else {
+    // three stages: tile t+2 is staged while tile t is multiplied, so a DMA has
+    // two steps to land
+    const uint32_t L2 = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(smem2));
+    if (nk > 0) {
+      prep();
+#pragma unroll
+      for (int q = 0; q < NLD; ++q) dma_q(q, L0);
+    }
+    if (nk > 1) {
+      prep();
+#pragma unroll
+      for (int q = 0; q < NLD; ++q) dma_q(q, L1);
+    }
+    int sc = 0;  // stage of tile t
+    for (int t = 0; t < nk; ++t) {
+      const char *cur = sc == 0 ? smem0 : (sc == 1 ? smem1 : smem2);
+      const uint32_t nxt = sc == 0 ? L2 : (sc == 1 ? L0 : L1);
+      // the wave's DMAs retire in issue order: at most tile t+1's may stay outstanding
+      if (t + 1 < nk) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NLD) : "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      lds_barrier();
+      step(cur, nxt, t + 2 < nk);
+      sc = sc == 2 ? 0 : sc + 1;
+    }
   }
 
-  // epilogue strips: waves 0-1 in stage 0, waves 2-3 in stage 1 (the first
+  // epilogue strips: the first half of the waves in stage 0, the rest in stage 1 (the first
   // __syncthreads inside the epilogue retires the last tile)
-  float *ep = (float *)(wid < 2 ? smem0 : smem1) + (wid & 1) * 32 * (WTN + 8);
-  epilogue<BM, BN, EPI, OUT_F32, true, DUAL>(d, acc, ep, lane, wm, wn, m0, n0, nlen, KSEG ? 0 : sn, split);
+  float *ep = (float *)(wid < NW / 2 ? smem0 : smem1) + (wid % (NW / 2)) * 32 * (WTN + 8);
+  epilogue<BM, BN, EPI, OUT_F32, true, DUAL, NW>(d, acc, ep, lane, wm, wn, m0, n0, nlen, KSEG ? 0 : sn, split);
 }
 
 template <int BM_, int BN_, bool A_KC_, bool B_KC_, int EPI_, bool OUT_F32_, bool KSEG_>
 struct Cfg {
   static constexpr int STAGE = 128 * (BM_ + BN_);
-  static __device__ __forceinline__ void run(const GemmDesc &d, int lid, char *s0, char *s1) {
-    dma_body<BM_, BN_, A_KC_, B_KC_, EPI_, OUT_F32_, KSEG_>(d, lid, s0, s1);
+  template <int NS>
+  static __device__ __forceinline__ void run(const GemmDesc &d, int lid, char *s0, char *s1, char *s2) {
+    dma_body<BM_, BN_, A_KC_, B_KC_, EPI_, OUT_F32_, KSEG_, 4, NS>(d, lid, s0, s1, s2);
   }
 };
 
-template <int BM, int BN, bool A_KC, bool B_KC, int EPI, bool OUT_F32, bool KSEG>
-__global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <int BM, int BN, bool A_KC, bool B_KC, int EPI, bool OUT_F32, bool KSEG, int RES>
+__global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(res_wgs(RES), res_wgs(RES))))
 gemm_dma_kernel(GemmDesc d) {
-  __shared__ __attribute__((aligned(1024))) char smem0[128 * (BM + BN)];
-  __shared__ __attribute__((aligned(1024))) char smem1[128 * (BM + BN)];
-  dma_body<BM, BN, A_KC, B_KC, EPI, OUT_F32, KSEG>(d, xcd_lid(blockIdx.x, gridDim.x), smem0, smem1);
+  static_assert(res_fits(BM, BN, RES), "LDS stages exceed the CU's 160 KB");
+  constexpr int S = 128 * (BM + BN), NS = res_stages(RES);
+  __shared__ __attribute__((aligned(1024))) char smem[NS * S];
+  dma_body<BM, BN, A_KC, B_KC, EPI, OUT_F32, KSEG, 4, NS>(d, xcd_lid(blockIdx.x, gridDim.x), smem, smem + S,
+                                                         NS == 3 ? smem + 2 * S : nullptr);
 }
 
 // Two independent products in one launch: workgroups [0, n1) compute the
@@ -922,19 +957,20 @@ gemm_dma_kernel(GemmDesc d) {
 // long-K weight gradient), so its workgroups are dispatched first and the short
 // tiles of the second fill the CUs around them.  Each range gets the XCD remap
 // when n1 is a multiple of 8 (then both ranges start on XCD 0).
-template <class C1, class C2>
-__global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <class C1, class C2, int RES>
+__global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(res_wgs(RES), res_wgs(RES))))
 gemm_dma_pair_kernel(GemmDesc d1, GemmDesc d2, int n1, int n2) {
-  constexpr int S = C1::STAGE > C2::STAGE ? C1::STAGE : C2::STAGE;
-  __shared__ __attribute__((aligned(1024))) char smem0[S];
-  __shared__ __attribute__((aligned(1024))) char smem1[S];
+  constexpr int S = C1::STAGE > C2::STAGE ? C1::STAGE : C2::STAGE, NS = res_stages(RES);
+  static_assert(NS * res_wgs(RES) * S <= 160 * 1024, "LDS stages exceed the CU's 160 KB");
+  __shared__ __attribute__((aligned(1024))) char smem[NS * S];
+  char *s2 = NS == 3 ? smem + 2 * S : nullptr;
   const int b = blockIdx.x;
   const bool remap = (n1 & 7) == 0;
   if (b < n1) {
-    C1::run(d1, remap ? xcd_lid(b, n1) : b, smem0, smem1);
+    C1::template run<NS>(d1, remap ? xcd_lid(b, n1) : b, smem, smem + S, s2);
   } else {
     const int r = b - n1;
-    C2::run(d2, remap ? xcd_lid(r, n2) : r, smem0, smem1);
+    C2::template run<NS>(d2, remap ? xcd_lid(r, n2) : r, smem, smem + S, s2);
   }
 }
 

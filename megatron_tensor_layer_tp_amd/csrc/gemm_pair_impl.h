@@ -9,58 +9,70 @@ namespace {
 template <int BM, int BN, int LAYOUT, int EPI, bool OUT_F32, bool KSEG>
 using CfgL = Cfg<BM, BN, LAYOUT != GEMM_TN, LAYOUT == GEMM_NT, EPI, OUT_F32, KSEG>;
 
-template <class C1, class C2>
+template <class C1, class C2, int RES>
 hipError_t go(const GemmDesc &d1, const GemmDesc &d2, bool dry, hipStream_t st) {
   if (dry) return hipSuccess;
   const int n1 = d1.tiles_m * d1.tiles_n * d1.splits;
   const int n2 = d2.tiles_m * d2.tiles_n * d2.splits;
   if (n1 + n2 == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_dma_pair_kernel<C1, C2>), dim3(n1 + n2), dim3(NTHREADS), 0, st, d1, d2, n1, n2);
+  hipLaunchKernelGGL((gemm_dma_pair_kernel<C1, C2, RES>), dim3(n1 + n2), dim3(NTHREADS), 0, st, d1, d2, n1, n2);
   return hipGetLastError();
 }
 
-template <int BN, int EPI, bool KSEG>
-using NT2 = CfgL<256, BN, GEMM_NT, EPI, false, KSEG>;
+// Built pairs: RES_TWO with 256-row tiles of 256 or 192 columns, RES_SHARED
+// with 128-row tiles of 192 or 128 columns, for both products.
+constexpr int pair_bm(int res) { return res == RES_SHARED ? 128 : 256; }
+constexpr int pair_wide(int res) { return res == RES_SHARED ? 192 : 256; }
+constexpr int pair_narrow(int res) { return res == RES_SHARED ? 128 : 192; }
 
-// first product fixed (C1): pick the second, an NT product with 256-row tiles.
-// Plain stores and the activation backward also take 192-column tiles.
-template <class C1>
+template <int BN, int EPI, bool KSEG, int RES>
+using NT2 = CfgL<pair_bm(RES), BN, GEMM_NT, EPI, false, KSEG>;
+
+template <class C1, int RES, int EPI, bool KSEG>
+hipError_t second_nt_bn(const GemmDesc &d1, const GemmDesc &d2, int bn, bool dry, hipStream_t st) {
+  if (bn == pair_wide(RES)) return go<C1, NT2<pair_wide(RES), EPI, KSEG, RES>, RES>(d1, d2, dry, st);
+  if (bn == pair_narrow(RES)) return go<C1, NT2<pair_narrow(RES), EPI, KSEG, RES>, RES>(d1, d2, dry, st);
+  return hipErrorNotSupported;
+}
+
+// first product fixed (C1): pick the second, an NT product with the same
+// residency: a store (also over K-segments), activation backward or SwiGLU
+// backward.
+template <class C1, int RES>
 hipError_t second_nt(const GemmDesc &d1, const GemmDesc &d2, const GemmVariant &v2, bool dry, hipStream_t st) {
-  if (v2.layout != GEMM_NT || v2.bm != 256 || v2.out_f32) return hipErrorNotSupported;
-  const int bn = v2.bn;
+  if (v2.layout != GEMM_NT || v2.bm != pair_bm(RES) || v2.res != RES || v2.out_f32) return hipErrorNotSupported;
   switch (v2.epi) {
   case EPI_STORE:
-    if (d2.kseg) {
-      if (bn == 256) return go<C1, NT2<256, EPI_STORE, true>>(d1, d2, dry, st);
-      if (bn == 128) return go<C1, NT2<128, EPI_STORE, true>>(d1, d2, dry, st);
-      return hipErrorNotSupported;
-    }
-    if (bn == 256) return go<C1, NT2<256, EPI_STORE, false>>(d1, d2, dry, st);
-    if (bn == 192) return go<C1, NT2<192, EPI_STORE, false>>(d1, d2, dry, st);
-    if (bn == 128) return go<C1, NT2<128, EPI_STORE, false>>(d1, d2, dry, st);
-    return hipErrorNotSupported;
+    if (d2.kseg) return second_nt_bn<C1, RES, EPI_STORE, true>(d1, d2, v2.bn, dry, st);
+    return second_nt_bn<C1, RES, EPI_STORE, false>(d1, d2, v2.bn, dry, st);
   case EPI_ACT_BWD:
     if (d2.kseg) return hipErrorNotSupported;
-    if (bn == 256) return go<C1, NT2<256, EPI_ACT_BWD, false>>(d1, d2, dry, st);
-    if (bn == 192) return go<C1, NT2<192, EPI_ACT_BWD, false>>(d1, d2, dry, st);
-    if (bn == 128) return go<C1, NT2<128, EPI_ACT_BWD, false>>(d1, d2, dry, st);
-    return hipErrorNotSupported;
+    return second_nt_bn<C1, RES, EPI_ACT_BWD, false>(d1, d2, v2.bn, dry, st);
   case EPI_SWIGLU_BWD:
     if (d2.kseg) return hipErrorNotSupported;
-    if (bn == 256) return go<C1, NT2<256, EPI_SWIGLU_BWD, false>>(d1, d2, dry, st);
-    if (bn == 128) return go<C1, NT2<128, EPI_SWIGLU_BWD, false>>(d1, d2, dry, st);
-    return hipErrorNotSupported;
+    return second_nt_bn<C1, RES, EPI_SWIGLU_BWD, false>(d1, d2, v2.bn, dry, st);
   default: return hipErrorNotSupported;
   }
 }
 
-// a TN first product (weight gradient) with 256-row tiles of 256, 192 or 128 columns
+template <int EPI1, bool F32, int RES>
+hipError_t first_tn_res(const GemmDesc &d1, const GemmVariant &v1, const GemmDesc &d2, const GemmVariant &v2,
+                        bool dry, hipStream_t st) {
+  constexpr int BM = pair_bm(RES);
+  if (v1.bm != BM) return hipErrorNotSupported;
+  if (v1.bn == pair_wide(RES))
+    return second_nt<CfgL<BM, pair_wide(RES), GEMM_TN, EPI1, F32, false>, RES>(d1, d2, v2, dry, st);
+  if (v1.bn == pair_narrow(RES))
+    return second_nt<CfgL<BM, pair_narrow(RES), GEMM_TN, EPI1, F32, false>, RES>(d1, d2, v2, dry, st);
+  return hipErrorNotSupported;
+}
+
+// a TN first product (weight gradient)
 template <int EPI1, bool F32>
 hipError_t first_tn(const GemmDesc &d1, const GemmVariant &v1, const GemmDesc &d2, const GemmVariant &v2, bool dry,
                     hipStream_t st) {
-  if (v1.bn == 256) return second_nt<CfgL<256, 256, GEMM_TN, EPI1, F32, false>>(d1, d2, v2, dry, st);
-  if (v1.bn == 192) return second_nt<CfgL<256, 192, GEMM_TN, EPI1, F32, false>>(d1, d2, v2, dry, st);
-  if (v1.bn == 128) return second_nt<CfgL<256, 128, GEMM_TN, EPI1, F32, false>>(d1, d2, v2, dry, st);
+  if (v1.res == RES_TWO) return first_tn_res<EPI1, F32, RES_TWO>(d1, v1, d2, v2, dry, st);
+  if (v1.res == RES_SHARED) return first_tn_res<EPI1, F32, RES_SHARED>(d1, v1, d2, v2, dry, st);
   return hipErrorNotSupported;
 }
 

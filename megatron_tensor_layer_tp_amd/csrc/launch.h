@@ -10,22 +10,41 @@ enum GemmLayout : int {
   GEMM_TN = 2,  // A [K][M], B [K][N]
 };
 
-// bf16 MFMA tiles: bm in {128, 256}, bn in {128, 192, 256} (192 not for the
-// dual or CE-statistics epilogues); vec = 16-byte loads are legal for
-// every operand (aligned pointers, leading dimensions and extents multiple of 8).
-hipError_t tp_launch_gemm_bf16(const GemmDesc &d, int layout, int epi, bool out_f32, int bm, int bn,
-                               bool vec, hipStream_t st);
-hipError_t tp_launch_splitk_reduce(const GemmDesc &d, bool out_f32, bool vec, hipStream_t st);
+// Residency of a bf16 DMA kernel on a CU: how many LDS stages each workgroup
+// keeps and how many workgroups share the CU.  Three stages give every tile
+// DMA two K steps to land (two stages wait on it after one); two workgroups per
+// CU run one's MFMAs under the other's load waits and epilogue.  Either needs
+// the stages to fit the CU's 160 KB of LDS.
+enum Residency : int {
+  RES_TWO = 0,     // 2 stages, one workgroup per CU
+  RES_THREE = 1,   // 3 stages, one workgroup per CU
+  RES_SHARED = 2,  // 2 stages, two workgroups per CU
+};
+constexpr int res_stages(int res) { return res == RES_THREE ? 3 : 2; }
+constexpr int res_wgs(int res) { return res == RES_SHARED ? 2 : 1; }
+constexpr bool res_fits(int bm, int bn, int res) {
+  return res_stages(res) * res_wgs(res) * 128 * (bm + bn) <= 160 * 1024;
+}
 
-// Two independent bf16 products in one launch (the second must not be split).
-// With dry = true nothing is launched: the return value only says whether the
-// pair of variants is built (hipSuccess) or not (hipErrorNotSupported).
+// One launchable bf16 kernel variant.  Built tiles (bm x bn, residency):
+// 256x256 and 256x192 with RES_TWO; 256x128, 128x256, 128x192 and 128x128 with
+// RES_THREE; 128x192 and 128x128 with RES_SHARED.  192 columns not for the dual
+// or CE-statistics epilogues.  vec = 16-byte loads are legal for every operand
+// (aligned pointers, leading dimensions and extents multiple of 8); without it
+// a 128x128 element-wise kernel runs whatever the tile fields say.
 struct GemmVariant {
   int layout, epi;
   bool out_f32;
-  int bm, bn;
+  int bm, bn, res;
   bool vec;
 };
+hipError_t tp_launch_gemm_bf16(const GemmDesc &d, const GemmVariant &v, hipStream_t st);
+hipError_t tp_launch_splitk_reduce(const GemmDesc &d, bool out_f32, bool vec, hipStream_t st);
+
+// Two independent bf16 products in one launch (the second must not be split),
+// both with the same residency.  With dry = true nothing is launched: the
+// return value only says whether the pair of variants is built (hipSuccess) or
+// not (hipErrorNotSupported).
 hipError_t tp_launch_gemm_pair(const GemmDesc &d1, const GemmVariant &v1, const GemmDesc &d2,
                                const GemmVariant &v2, bool dry, hipStream_t st);
 // the pairs whose first product is a TN split-K partial (called by tp_launch_gemm_pair)

@@ -15,6 +15,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
+#include <vector>
 #include <string>
 
 #include "../../include/tpshard.h"
@@ -101,7 +103,7 @@ struct Checker {
 
 // ---------------------------------------------------------------- planning
 struct Plan {
-  int bm = 128, bn = 128, splits = 1, kt_per_split = 1, tiles_m = 0, tiles_n = 0;
+  int bm = 128, bn = 128, res = RES_THREE, splits = 1, kt_per_split = 1, tiles_m = 0, tiles_n = 0;
   bool vec = true;
   size_t ws_bytes = 0;  // split-K partials
 };
@@ -115,8 +117,6 @@ struct Spec {               // one product, described before planning
   bool kseg = false;
   bool dual = false;
   bool can_split = false;   // a workspace for split-K partials is available
-  bool bm256 = false;       // only 256-row tiles (the shapes built for paired launches)
-  bool no192 = false;       // no 192-column tiles
   int64_t seg[TP_MAX_SEG] = {0, 0, 0};  // N-extents (N-segments) or K-extents (K-segments)
   int64_t N = 0;            // total N (kseg or single segment)
   int64_t lds[12] = {};     // every leading dimension involved
@@ -141,20 +141,110 @@ int64_t ktiles(const Spec &s) {
   return t;
 }
 
-// Relative MFMA efficiency of each tile shape per FLOP (larger tiles re-read
-// less and keep the LDS traffic per MFMA lower); 128x128 runs two workgroups
-// per CU.  Measured on MI355X in full rounds of an 8192x8192x3584 product,
-// relative to 256x256.
-double tile_eff(int bm, int bn) {
-  if (bm == 256 && bn == 256) return 1.0;
-  if (bm == 256 && bn == 192) return 0.9;
-  if (bm == 128 && bn == 192) return 0.65;
-  if (bm == 128 && bn == 128) return 0.53;
-  return 0.78;  // 256x128, 128x256
+// ---- cost model of the bf16 DMA kernels (microseconds, measured on MI355X)
+// For each built (tile, residency) variant: the time of one 64-deep K step of a
+// block when every slot of its CU is busy (`step`), the same over launches of
+// three or more rounds (`step_long`: two workgroups per CU then lose more to
+// L2 misses), and when a two-workgroup variant has its CU to itself
+// (`alone`); the per-block prologue + bf16-store epilogue (`fixed`); and the
+// extra cost of the first round of a launch (`first`).  Fitted from K sweeps
+// of one- and two-round NN products and from full products of K = 8192.
+struct TileCost {
+  int bm, bn, res;
+  double step, step_long, alone, fixed, first;
+};
+constexpr TileCost kTiles[] = {
+    {256, 256, RES_TWO, 1.58, 1.58, 1.58, 11.3, 1.2},     {256, 192, RES_TWO, 1.26, 1.26, 1.26, 10.0, 1.0},
+    {256, 128, RES_THREE, 0.91, 0.91, 0.91, 10.0, 0.5},   {128, 256, RES_THREE, 0.91, 0.91, 0.91, 10.0, 0.7},
+    {128, 192, RES_THREE, 0.72, 0.72, 0.72, 7.8, 1.6},    {128, 128, RES_THREE, 0.57, 0.57, 0.57, 6.0, 0.3},
+    {128, 192, RES_SHARED, 1.15, 1.60, 0.78, 5.4, 9.6},   {128, 128, RES_SHARED, 0.975, 1.35, 0.65, 3.2, 3.6},
+};
+constexpr double kLaunchUs = 2.0;     // one more kernel in the stream
+constexpr double kReduceBw = 4.0e6;   // split-K reduction traffic, bytes per microsecond
+
+// extra epilogue time per output element of a block, beyond a bf16 store
+double epi_cost(int epi, bool out_f32, int res) {
+  const bool sh = res == RES_SHARED;
+  switch (epi) {
+  case EPI_ACT_FWD: return sh ? 1.3e-4 : 1.7e-4;
+  case EPI_ACT_BWD: return sh ? 2.4e-4 : 2.9e-4;
+  case EPI_SWIGLU_FWD: return sh ? 1.6e-4 : 2.0e-4;
+  case EPI_SWIGLU_BWD: return sh ? 3.3e-4 : 4.0e-4;
+  case EPI_PARTIAL: return sh ? 0.3e-4 : 0.7e-4;
+  case EPI_CE_STATS: return 1.0e-4;
+  default: return out_f32 ? (sh ? 0.2e-4 : 0.5e-4) : 0.0;
+  }
 }
 
-Plan plan_bf16(const Spec &s) {
-  Plan p;
+bool variant_built(int bm, int bn, int res, bool dual, int epi) {
+  if (bn == 192 && (dual || epi == EPI_CE_STATS)) return false;
+  for (const TileCost &t : kTiles)
+    if (t.bm == bm && t.bn == bn && t.res == res) return true;
+  return false;
+}
+const TileCost &tile_cost(int bm, int bn, int res) {
+  for (const TileCost &t : kTiles)
+    if (t.bm == bm && t.bn == bn && t.res == res) return t;
+  return kTiles[0];
+}
+
+// duration of one block of the planned product (kps K steps) in a launch of
+// `nb` blocks in all
+double block_us(const Spec &s, const Plan &p, int64_t nb) {
+  const TileCost &t = tile_cost(p.bm, p.bn, p.res);
+  const int64_t slots = (int64_t)kCUs * res_wgs(p.res);
+  const double step = nb <= kCUs ? t.alone : (nb > 2 * slots ? t.step_long : t.step);
+  const int epi = p.splits > 1 ? (int)EPI_PARTIAL : s.epi;
+  return p.kt_per_split * step + t.fixed + epi_cost(epi, p.splits > 1 || s.out_f32, p.res) * p.bm * p.bn;
+}
+int64_t plan_blocks(const Plan &p) { return (int64_t)p.tiles_m * p.tiles_n * p.splits; }
+int plan_slots(const Plan &p) { return kCUs * res_wgs(p.res); }
+
+// the split-K reduction pass: read every partial, write the output
+double reduce_us(const Spec &s, const Plan &p) {
+  if (p.splits <= 1) return 0.0;
+  const double bytes = (double)s.M * s.N * (4.0 * p.splits + (s.out_f32 ? 4.0 : 2.0));
+  return kLaunchUs + bytes / kReduceBw;
+}
+
+// greedy dispatch of n1 blocks of d1 then n2 blocks of d2 over `slots`
+// workgroup slots (each new block to the earliest free slot): the makespan.
+// Slots free at the same time are handled as one group, so the loop runs about
+// once per round.
+double list_makespan(int64_t n1, double d1, int64_t n2, double d2, int slots) {
+  std::map<double, int64_t> free_at{{0.0, slots}};
+  double end = 0.0;
+  auto run = [&](int64_t n, double d) {
+    while (n > 0) {
+      const auto it = free_at.begin();
+      const double t = it->first;
+      const int64_t c = it->second;
+      free_at.erase(it);
+      const int64_t k = std::min(c, n);
+      n -= k;
+      if (c > k) free_at[t] += c - k;
+      free_at[t + d] += k;
+      end = std::max(end, t + d);
+    }
+  };
+  run(n1, d1);
+  run(n2, d2);
+  return end;
+}
+
+// estimated time of one planned product launched alone (with its reduction)
+double plan_us(const Spec &s, const Plan &p) {
+  const int64_t nb = plan_blocks(p);
+  if (nb == 0) return 0.0;
+  const int slots = plan_slots(p);
+  const double d = block_us(s, p, nb);
+  const double rounds = (double)((nb + slots - 1) / slots);
+  return kLaunchUs + tile_cost(p.bm, p.bn, p.res).first + rounds * d + reduce_us(s, p);
+}
+
+// every built variant of the product with the split counts worth trying
+template <class F>
+void for_each_plan(const Spec &s, F &&f) {
   bool vec = true;
   // 16-byte DMA / buffer loads: leading dimensions multiples of 8 elements, and
   // a 256-row tile's byte span addressable with 32-bit buffer offsets
@@ -167,47 +257,43 @@ Plan plan_bf16(const Spec &s) {
     vec &= s.K % 8 == 0;
     for (int i = 0; i < s.nseg; ++i) vec &= s.seg[i] % 8 == 0;
   }
-  p.vec = vec;
   const int64_t KT = ktiles(s);
   const bool can_split = s.can_split && s.epi == EPI_STORE && !s.dual && KT >= 8;
-  // 192 columns: N = 768, 1536 or 6144 then fills the 256 CUs in whole rounds
-  static const int shapes[6][2] = {{256, 256}, {256, 192}, {256, 128}, {128, 256}, {128, 192}, {128, 128}};
-  const bool no192 = s.no192 || s.dual || s.epi == EPI_CE_STATS;
-  double best = 1e300;
-  for (auto &sh : shapes) {
-    const int bm = sh[0], bn = sh[1];
-    if (!vec && !(bm == 128 && bn == 128)) continue;
-    if (s.bm256 && bm != 256) continue;
-    if (no192 && bn == 192) continue;
-    const int64_t tm = cdiv(s.M, bm), tn = ntiles_n(s, bn);
-    const int64_t tiles = tm * tn;
-    const int slots = (bm == 128 && bn == 128) ? 2 * kCUs : kCUs;
-    const double per_slot_rate = tile_eff(bm, bn) * ((bm == 128 && bn == 128) ? 0.5 : 1.0);
-    for (int sp = 1; sp <= (can_split ? 8 : 1); ++sp) {
-      if (sp > 1 && (KT / sp < 4 || tiles * (sp - 1) >= slots)) break;
+  for (const TileCost &t : kTiles) {
+    Plan p;
+    p.vec = vec;
+    p.bm = t.bm;
+    p.bn = t.bn;
+    p.res = t.res;
+    if (!vec) {  // the element-wise kernel: 128x128, one workgroup per CU
+      if (!(t.bm == 128 && t.bn == 128 && t.res == RES_THREE)) continue;
+    } else if (!variant_built(t.bm, t.bn, t.res, s.dual, s.epi)) {
+      continue;
+    }
+    p.tiles_m = (int)cdiv(s.M, p.bm);
+    p.tiles_n = (int)ntiles_n(s, p.bn);
+    for (int sp = 1; sp <= (can_split && vec ? 16 : 1); ++sp) {
       const int64_t kps = cdiv(std::max<int64_t>(KT, 1), sp);
-      const int64_t nblk = tiles * sp;
-      const double waves = (double)cdiv(nblk, slots);
-      // time in units of one 128x128x64 MFMA step on a full CU
-      double t = waves * kps * (bm * bn) / (128.0 * 128.0) / per_slot_rate;
-      if (sp > 1) {
-        // partial writes + the reduction pass, ~1 MFMA step per 4 KB of fp32 traffic
-        const double bytes = (double)s.M * s.N * 4.0 * (2.0 * sp + 1.0);
-        t += bytes / kCUs / 4096.0 + 4.0;
-      }
-      if (t < best * 0.999) {
-        best = t;
-        p.bm = bm;
-        p.bn = bn;
-        p.splits = sp;
-        p.kt_per_split = (int)kps;
-        p.tiles_m = (int)tm;
-        p.tiles_n = (int)tn;
-      }
+      if (sp > 1 && (kps < 4 || cdiv(KT, kps) < sp)) break;
+      p.splits = sp;
+      p.kt_per_split = (int)kps;
+      p.ws_bytes = sp > 1 ? (size_t)sp * s.M * s.N * sizeof(float) : 0;
+      f(p);
     }
   }
-  if (p.splits > 1) p.ws_bytes = (size_t)p.splits * s.M * s.N * sizeof(float);
-  return p;
+}
+
+Plan plan_bf16(const Spec &s) {
+  Plan best;
+  double best_t = 1e300;
+  for_each_plan(s, [&](const Plan &p) {
+    const double t = plan_us(s, p);
+    if (t < best_t * 0.999) {
+      best_t = t;
+      best = p;
+    }
+  });
+  return best;
 }
 
 Plan plan_f32(const Spec &s) {
@@ -295,6 +381,7 @@ GemmVariant variant(const Spec &s, const Plan &p) {
   v.out_f32 = p.splits > 1 ? true : s.out_f32;
   v.bm = p.bm;
   v.bn = p.bn;
+  v.res = p.res;
   v.vec = p.vec;
   return v;
 }
@@ -308,7 +395,7 @@ int run_planned(const Spec &s, const Plan &p, const Ptrs &q, int dt, void *ws, h
     e = tp_launch_gemm_f32(d, s.layout, s.epi, st);
   } else {
     const GemmVariant v = variant(s, p);
-    e = tp_launch_gemm_bf16(d, v.layout, v.epi, v.out_f32, p.bm, p.bn, p.vec, st);
+    e = tp_launch_gemm_bf16(d, v, st);
     if (e == hipSuccess && p.splits > 1) e = tp_launch_splitk_reduce(d, s.out_f32, p.vec, st);
   }
   if (e != hipSuccess) return fail(TP_EHIP, "%s: %s", what, hipGetErrorString(e));
@@ -331,28 +418,43 @@ struct PairPlan {
 
 PairPlan pair_plan(const Spec &s1, const Spec &s2, int dt) {
   PairPlan r;
-  if (dt == TP_DT_BF16) {
-    Spec a = s1, b = s2;
-    a.bm256 = b.bm256 = true;
-    b.can_split = false;
-    // 192-column tiles are built for TN first products and for NT stores / activation
-    // backward as the second
-    a.no192 = a.layout != GEMM_TN || a.kseg;
-    b.no192 = b.layout != GEMM_NT || b.kseg || (b.epi != EPI_STORE && b.epi != EPI_ACT_BWD);
-    r.p1 = plan_bf16(a);
-    r.p2 = plan_bf16(b);
-    GemmDesc d1, d2;
-    std::memset(&d1, 0, sizeof d1);
-    std::memset(&d2, 0, sizeof d2);
-    d1.kseg = a.kseg;
-    d2.kseg = b.kseg;
-    r.paired = r.p1.vec && r.p2.vec &&
-               tp_launch_gemm_pair(d1, variant(a, r.p1), d2, variant(b, r.p2), true, nullptr) == hipSuccess;
-  }
-  if (!r.paired) {
+  if (dt != TP_DT_BF16) {
     r.p1 = plan(s1, dt);
     r.p2 = plan(s2, dt);
+    return r;
   }
+  // apart: each with its own best plan
+  r.p1 = plan_bf16(s1);
+  r.p2 = plan_bf16(s2);
+  double best = plan_us(s1, r.p1) + plan_us(s2, r.p2);
+  // together: every built pair of variants with one residency, the first
+  // possibly split along K
+  Spec b = s2;
+  b.can_split = false;
+  std::vector<Plan> c2;
+  for_each_plan(b, [&](const Plan &p) { c2.push_back(p); });
+  GemmDesc d1, d2;
+  std::memset(&d1, 0, sizeof d1);
+  std::memset(&d2, 0, sizeof d2);
+  d1.kseg = s1.kseg;
+  d2.kseg = s2.kseg;
+  for_each_plan(s1, [&](const Plan &p1) {
+    for (const Plan &p2 : c2) {
+      if (!p1.vec || !p2.vec || p1.res != p2.res) continue;
+      if (tp_launch_gemm_pair(d1, variant(s1, p1), d2, variant(b, p2), true, nullptr) != hipSuccess) continue;
+      const int64_t n1 = plan_blocks(p1), n2 = plan_blocks(p2);
+      const double t = kLaunchUs +
+                       std::max(tile_cost(p1.bm, p1.bn, p1.res).first, tile_cost(p2.bm, p2.bn, p2.res).first) +
+                       list_makespan(n1, block_us(s1, p1, n1 + n2), n2, block_us(b, p2, n1 + n2), plan_slots(p1)) +
+                       reduce_us(s1, p1);
+      if (t < best * 0.999) {
+        best = t;
+        r.paired = true;
+        r.p1 = p1;
+        r.p2 = p2;
+      }
+    }
+  });
   return r;
 }
 
@@ -1001,7 +1103,7 @@ int tp_lm_head_ce_fwd(int dt, int64_t s, int64_t h, int64_t Vs, int64_t vocab_st
   q.ai0 = target;
   GemmDesc d = make_desc(L.g, q, L.p, TP_DT_BF16, ws);
   d.vstart = vocab_start;
-  hipError_t e = tp_launch_gemm_bf16(d, GEMM_NN, EPI_CE_STATS, true, L.p.bm, L.p.bn, L.p.vec, st);
+  hipError_t e = tp_launch_gemm_bf16(d, variant(L.g, L.p), st);
   if (e == hipSuccess)
     e = tp_launch_ce_merge((const float *)ws, L.parts, L.width, s, Vs, vocab_start, target, lmax, lsumexp, tlogit,
                            st);
