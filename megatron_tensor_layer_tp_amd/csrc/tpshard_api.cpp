@@ -14,6 +14,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <vector>
@@ -242,6 +243,25 @@ double plan_us(const Spec &s, const Plan &p) {
   return kLaunchUs + tile_cost(p.bm, p.bn, p.res).first + rounds * d + reduce_us(s, p);
 }
 
+// TP_GEMM_VARIANT="BMxBN:two|three|shared" restricts every bf16 product that has
+// that variant built (and 16-byte operands) to it, split counts still chosen by
+// the cost model; the parity tests use it to run each variant on the same sizes.
+struct ForcedVariant {
+  bool on = false;
+  int bm = 0, bn = 0, res = 0;
+};
+ForcedVariant forced_variant() {
+  ForcedVariant f;
+  const char *e = std::getenv("TP_GEMM_VARIANT");
+  if (e == nullptr || *e == 0) return f;
+  char r[16] = {0};
+  if (std::sscanf(e, "%dx%d:%15s", &f.bm, &f.bn, r) != 3) return f;
+  const std::string rs(r);
+  f.res = rs == "two" ? RES_TWO : rs == "three" ? RES_THREE : rs == "shared" ? RES_SHARED : -1;
+  f.on = f.res >= 0;
+  return f;
+}
+
 // every built variant of the product with the split counts worth trying
 template <class F>
 void for_each_plan(const Spec &s, F &&f) {
@@ -259,7 +279,10 @@ void for_each_plan(const Spec &s, F &&f) {
   }
   const int64_t KT = ktiles(s);
   const bool can_split = s.can_split && s.epi == EPI_STORE && !s.dual && KT >= 8;
+  ForcedVariant fv = forced_variant();
+  if (fv.on && !(vec && variant_built(fv.bm, fv.bn, fv.res, s.dual, s.epi))) fv.on = false;
   for (const TileCost &t : kTiles) {
+    if (fv.on && !(t.bm == fv.bm && t.bn == fv.bn && t.res == fv.res)) continue;
     Plan p;
     p.vec = vec;
     p.bm = t.bm;

@@ -117,8 +117,9 @@ EXACT_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("s,h,ft", EXACT_SHAPES)
-def test_integer_bf16_exact(oracle_mod, s, h, ft):
+def integer_exact_case(oracle_mod, s, h, ft):
+    """Integer inputs in {-1,0,1}, bf16 storage: the GPU must match the oracle
+    rounded to bf16 exactly where the kernels store."""
     g = np.random.default_rng(s * 7 + h)
     X, W1, W2, dY = (g.integers(-1, 2, size=sh).astype(np.float32)
                      for sh in ((s, h), (h, ft), (ft, h), (s, h)))
@@ -135,6 +136,11 @@ def test_integer_bf16_exact(oracle_mod, s, h, ft):
         got = host_f64(t)
         bad = np.argwhere(got != want[k])
         assert bad.size == 0, (k, bad[:5], got[tuple(bad[0])], want[k][tuple(bad[0])])
+
+
+@pytest.mark.parametrize("s,h,ft", EXACT_SHAPES)
+def test_integer_bf16_exact(oracle_mod, s, h, ft):
+    integer_exact_case(oracle_mod, s, h, ft)
 
 
 # ---------------------------------------------------------------- floating point
