@@ -8,14 +8,15 @@ template <int BM, int BN, bool A_KC, bool B_KC, int EPI, bool OUT_F32, bool KSEG
 hipError_t launch_dma(const GemmDesc &d, hipStream_t st) {
   const int nblk = d.tiles_m * d.tiles_n * d.splits;
   if (nblk == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, A_KC, B_KC, EPI, OUT_F32, KSEG, RES>), dim3(nblk), dim3(NTHREADS), 0,
-                     st, d);
+  hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, A_KC, B_KC, EPI, OUT_F32, KSEG, RES>), dim3(nblk),
+                     dim3(64 * res_waves(RES)), 0, st, d);
   return hipGetLastError();
 }
 
 // The built (tile, residency) variants: 256x256 and 256x192 with two stages;
-// 256x128, 128x256, 128x192 and 128x128 with three; 128x192 and 128x128 also
-// two workgroups per CU.  192-column tiles not for the dual or CE epilogues.
+// 256x256 with 8 waves (not the dual epilogue); 256x128, 128x256, 128x192 and
+// 128x128 with three; 128x192 and 128x128 also two workgroups per CU.
+// 192-column tiles not for the dual or CE epilogues.
 template <bool A_KC, bool B_KC, int EPI, bool OUT_F32, bool KSEG>
 hipError_t launch_shape_k(const GemmDesc &d, int bm, int bn, int res, hipStream_t st, bool vec) {
   if (!vec) {  // element-wise loads (odd sizes / leading dimensions): 128x128 tiles only
@@ -31,6 +32,10 @@ hipError_t launch_shape_k(const GemmDesc &d, int bm, int bn, int res, hipStream_
     if (bm == 256 && bn == 256) return launch_dma<256, 256, A_KC, B_KC, EPI, OUT_F32, KSEG, RES_TWO>(d, st);
     if constexpr (W192)
       if (bm == 256 && bn == 192) return launch_dma<256, 192, A_KC, B_KC, EPI, OUT_F32, KSEG, RES_TWO>(d, st);
+    break;
+  case RES_WAVES8:
+    if constexpr (EPI != EPI_SWIGLU_FWD)
+      if (bm == 256 && bn == 256) return launch_dma<256, 256, A_KC, B_KC, EPI, OUT_F32, KSEG, RES_WAVES8>(d, st);
     break;
   case RES_THREE:
     if (bm == 256 && bn == 128) return launch_dma<256, 128, A_KC, B_KC, EPI, OUT_F32, KSEG, RES_THREE>(d, st);

@@ -334,7 +334,7 @@ __device__ __forceinline__ float row_sum(float v) {
 // holds the target.  Every lane must call it (cross-lane moves); rows >= M
 // write nothing.
 template <int LPR>
-__device__ __forceinline__ void ce_stats8(const GemmDesc &d, int gm, int gn, int nlen, int part, int lane,
+__device__ __forceinline__ void ce_stats8(const GemmDesc &d, int gm, int gn, int nlen, int part, int P, int lane,
                                           const float *x) {
   static_assert(LPR == 8 || LPR == 16, "row reductions span 8 or 16 lanes");
   constexpr float LOG2E = 1.4426950408889634f;
@@ -353,7 +353,6 @@ __device__ __forceinline__ void ce_stats8(const GemmDesc &d, int gm, int gn, int
   }
   se = row_sum<LPR>(se);
   if (gm < d.M) {
-    const int P = 2 * d.tiles_n;
     float *w = d.ws + (int64_t)gm * 3 * P + part;
     if (lane % LPR == 0) {
       w[0] = mx;
@@ -420,7 +419,8 @@ __device__ __forceinline__ void epilogue(const GemmDesc &d, f32x16 (&acc)[BM / 6
       const int gm = m0 + wm * WTM + fm * 32 + r;
       const int gn = col_base + c;
       if constexpr (EPI == EPI_CE_STATS) {
-        ce_stats8<LPR>(d, gm, gn, nlen, col_base / WTN, lane, x);
+        // one part per wave column of every tile: BN / WTN parts per tile
+        ce_stats8<LPR>(d, gm, gn, nlen, col_base / WTN, (BN / WTN) * d.tiles_n, lane, x);
       } else {
         if (live && gm < d.M && gn < nlen) epi8<EPI, OUT_F32, VEC>(d, gm, gn, nlen, sc, split, x, u);
       }
@@ -936,20 +936,23 @@ __device__ __forceinline__ void dma_body(const GemmDesc &d, int lid, char *smem0
 template <int BM_, int BN_, bool A_KC_, bool B_KC_, int EPI_, bool OUT_F32_, bool KSEG_>
 struct Cfg {
   static constexpr int STAGE = 128 * (BM_ + BN_);
-  template <int NS>
+  template <int NS, int NW>
   static __device__ __forceinline__ void run(const GemmDesc &d, int lid, char *s0, char *s1, char *s2) {
-    dma_body<BM_, BN_, A_KC_, B_KC_, EPI_, OUT_F32_, KSEG_, 4, NS>(d, lid, s0, s1, s2);
+    dma_body<BM_, BN_, A_KC_, B_KC_, EPI_, OUT_F32_, KSEG_, NW, NS>(d, lid, s0, s1, s2);
   }
 };
 
+// waves per SIMD of a residency (4 SIMDs per CU)
+constexpr int res_wpe(int res) { return res_wgs(res) * res_waves(res) / 4; }
+
 template <int BM, int BN, bool A_KC, bool B_KC, int EPI, bool OUT_F32, bool KSEG, int RES>
-__global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(res_wgs(RES), res_wgs(RES))))
-gemm_dma_kernel(GemmDesc d) {
+__global__ void __launch_bounds__(64 * res_waves(RES))
+__attribute__((amdgpu_waves_per_eu(res_wpe(RES), res_wpe(RES)))) gemm_dma_kernel(GemmDesc d) {
   static_assert(res_fits(BM, BN, RES), "LDS stages exceed the CU's 160 KB");
   constexpr int S = 128 * (BM + BN), NS = res_stages(RES);
   __shared__ __attribute__((aligned(1024))) char smem[NS * S];
-  dma_body<BM, BN, A_KC, B_KC, EPI, OUT_F32, KSEG, 4, NS>(d, xcd_lid(blockIdx.x, gridDim.x), smem, smem + S,
-                                                         NS == 3 ? smem + 2 * S : nullptr);
+  dma_body<BM, BN, A_KC, B_KC, EPI, OUT_F32, KSEG, res_waves(RES), NS>(
+      d, xcd_lid(blockIdx.x, gridDim.x), smem, smem + S, NS == 3 ? smem + 2 * S : nullptr);
 }
 
 // Two independent products in one launch: workgroups [0, n1) compute the
@@ -958,8 +961,9 @@ gemm_dma_kernel(GemmDesc d) {
 // tiles of the second fill the CUs around them.  Each range gets the XCD remap
 // when n1 is a multiple of 8 (then both ranges start on XCD 0).
 template <class C1, class C2, int RES>
-__global__ void __launch_bounds__(NTHREADS) __attribute__((amdgpu_waves_per_eu(res_wgs(RES), res_wgs(RES))))
-gemm_dma_pair_kernel(GemmDesc d1, GemmDesc d2, int n1, int n2) {
+__global__ void __launch_bounds__(64 * res_waves(RES))
+__attribute__((amdgpu_waves_per_eu(res_wpe(RES), res_wpe(RES)))) gemm_dma_pair_kernel(GemmDesc d1, GemmDesc d2,
+                                                                                      int n1, int n2) {
   constexpr int S = C1::STAGE > C2::STAGE ? C1::STAGE : C2::STAGE, NS = res_stages(RES);
   static_assert(NS * res_wgs(RES) * S <= 160 * 1024, "LDS stages exceed the CU's 160 KB");
   __shared__ __attribute__((aligned(1024))) char smem[NS * S];
@@ -967,10 +971,10 @@ gemm_dma_pair_kernel(GemmDesc d1, GemmDesc d2, int n1, int n2) {
   const int b = blockIdx.x;
   const bool remap = (n1 & 7) == 0;
   if (b < n1) {
-    C1::template run<NS>(d1, remap ? xcd_lid(b, n1) : b, smem, smem + S, s2);
+    C1::template run<NS, res_waves(RES)>(d1, remap ? xcd_lid(b, n1) : b, smem, smem + S, s2);
   } else {
     const int r = b - n1;
-    C2::template run<NS>(d2, remap ? xcd_lid(r, n2) : r, smem, smem + S, s2);
+    C2::template run<NS, res_waves(RES)>(d2, remap ? xcd_lid(r, n2) : r, smem, smem + S, s2);
   }
 }
 

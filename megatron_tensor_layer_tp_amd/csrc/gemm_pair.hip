@@ -5,8 +5,8 @@
 //
 // Supported pairs (first = the long-K product, second = the short-K one), both
 // with 16-byte-aligned operands and one residency: RES_TWO with 256-row tiles
-// of 256 or 192 columns, RES_SHARED (two workgroups per CU) with 128-row tiles
-// of 192 or 128 columns:
+// of 256 or 192 columns, RES_WAVES8 with 256x256 tiles, RES_SHARED (two
+// workgroups per CU) with 128-row tiles of 192 or 128 columns:
 //   first  TN store (bf16) or TN split-K partial (fp32; gemm_pair_partial.hip);
 //   second NT store (also over K-segments), NT activation backward or NT SwiGLU
 //          backward;
@@ -22,8 +22,9 @@ hipError_t second_nn(const GemmDesc &d1, const GemmDesc &d2, const GemmVariant &
     return hipErrorNotSupported;
   if (v2.bn == pair_wide(RES))
     return go<C1, CfgL<BM, pair_wide(RES), GEMM_NN, EPI_STORE, false, false>, RES>(d1, d2, dry, st);
-  if (v2.bn == pair_narrow(RES))
-    return go<C1, CfgL<BM, pair_narrow(RES), GEMM_NN, EPI_STORE, false, false>, RES>(d1, d2, dry, st);
+  if constexpr (pair_narrow(RES) != pair_wide(RES))
+    if (v2.bn == pair_narrow(RES))
+      return go<C1, CfgL<BM, pair_narrow(RES), GEMM_NN, EPI_STORE, false, false>, RES>(d1, d2, dry, st);
   return hipErrorNotSupported;
 }
 
@@ -34,8 +35,9 @@ hipError_t first_nn(const GemmDesc &d1, const GemmVariant &v1, const GemmDesc &d
   if (v1.bm != BM) return hipErrorNotSupported;
   if (v1.bn == pair_wide(RES))
     return second_nn<CfgL<BM, pair_wide(RES), GEMM_NN, EPI_STORE, false, false>, RES>(d1, d2, v2, dry, st);
-  if (v1.bn == pair_narrow(RES))
-    return second_nn<CfgL<BM, pair_narrow(RES), GEMM_NN, EPI_STORE, false, false>, RES>(d1, d2, v2, dry, st);
+  if constexpr (pair_narrow(RES) != pair_wide(RES))
+    if (v1.bn == pair_narrow(RES))
+      return second_nn<CfgL<BM, pair_narrow(RES), GEMM_NN, EPI_STORE, false, false>, RES>(d1, d2, v2, dry, st);
   return hipErrorNotSupported;
 }
 
@@ -51,6 +53,7 @@ hipError_t tp_launch_gemm_pair(const GemmDesc &d1, const GemmVariant &v1, const 
   }
   if (v1.layout == GEMM_NN && v1.epi == EPI_STORE && !v1.out_f32) {
     if (v1.res == RES_TWO) return first_nn<RES_TWO>(d1, v1, d2, v2, dry, st);
+    if (v1.res == RES_WAVES8) return first_nn<RES_WAVES8>(d1, v1, d2, v2, dry, st);
     if (v1.res == RES_SHARED) return first_nn<RES_SHARED>(d1, v1, d2, v2, dry, st);
   }
   return hipErrorNotSupported;

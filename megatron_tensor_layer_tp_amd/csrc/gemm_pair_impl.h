@@ -15,15 +15,17 @@ hipError_t go(const GemmDesc &d1, const GemmDesc &d2, bool dry, hipStream_t st) 
   const int n1 = d1.tiles_m * d1.tiles_n * d1.splits;
   const int n2 = d2.tiles_m * d2.tiles_n * d2.splits;
   if (n1 + n2 == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_dma_pair_kernel<C1, C2, RES>), dim3(n1 + n2), dim3(NTHREADS), 0, st, d1, d2, n1, n2);
+  hipLaunchKernelGGL((gemm_dma_pair_kernel<C1, C2, RES>), dim3(n1 + n2), dim3(64 * res_waves(RES)), 0, st, d1, d2,
+                     n1, n2);
   return hipGetLastError();
 }
 
-// Built pairs: RES_TWO with 256-row tiles of 256 or 192 columns, RES_SHARED
-// with 128-row tiles of 192 or 128 columns, for both products.
+// Built pairs: RES_TWO with 256-row tiles of 256 or 192 columns, RES_WAVES8
+// with 256x256 tiles, RES_SHARED with 128-row tiles of 192 or 128 columns, for
+// both products.
 constexpr int pair_bm(int res) { return res == RES_SHARED ? 128 : 256; }
 constexpr int pair_wide(int res) { return res == RES_SHARED ? 192 : 256; }
-constexpr int pair_narrow(int res) { return res == RES_SHARED ? 128 : 192; }
+constexpr int pair_narrow(int res) { return res == RES_SHARED ? 128 : res == RES_WAVES8 ? 256 : 192; }
 
 template <int BN, int EPI, bool KSEG, int RES>
 using NT2 = CfgL<pair_bm(RES), BN, GEMM_NT, EPI, false, KSEG>;
@@ -31,7 +33,8 @@ using NT2 = CfgL<pair_bm(RES), BN, GEMM_NT, EPI, false, KSEG>;
 template <class C1, int RES, int EPI, bool KSEG>
 hipError_t second_nt_bn(const GemmDesc &d1, const GemmDesc &d2, int bn, bool dry, hipStream_t st) {
   if (bn == pair_wide(RES)) return go<C1, NT2<pair_wide(RES), EPI, KSEG, RES>, RES>(d1, d2, dry, st);
-  if (bn == pair_narrow(RES)) return go<C1, NT2<pair_narrow(RES), EPI, KSEG, RES>, RES>(d1, d2, dry, st);
+  if constexpr (pair_narrow(RES) != pair_wide(RES))
+    if (bn == pair_narrow(RES)) return go<C1, NT2<pair_narrow(RES), EPI, KSEG, RES>, RES>(d1, d2, dry, st);
   return hipErrorNotSupported;
 }
 
@@ -62,8 +65,9 @@ hipError_t first_tn_res(const GemmDesc &d1, const GemmVariant &v1, const GemmDes
   if (v1.bm != BM) return hipErrorNotSupported;
   if (v1.bn == pair_wide(RES))
     return second_nt<CfgL<BM, pair_wide(RES), GEMM_TN, EPI1, F32, false>, RES>(d1, d2, v2, dry, st);
-  if (v1.bn == pair_narrow(RES))
-    return second_nt<CfgL<BM, pair_narrow(RES), GEMM_TN, EPI1, F32, false>, RES>(d1, d2, v2, dry, st);
+  if constexpr (pair_narrow(RES) != pair_wide(RES))
+    if (v1.bn == pair_narrow(RES))
+      return second_nt<CfgL<BM, pair_narrow(RES), GEMM_TN, EPI1, F32, false>, RES>(d1, d2, v2, dry, st);
   return hipErrorNotSupported;
 }
 
@@ -72,6 +76,7 @@ template <int EPI1, bool F32>
 hipError_t first_tn(const GemmDesc &d1, const GemmVariant &v1, const GemmDesc &d2, const GemmVariant &v2, bool dry,
                     hipStream_t st) {
   if (v1.res == RES_TWO) return first_tn_res<EPI1, F32, RES_TWO>(d1, v1, d2, v2, dry, st);
+  if (v1.res == RES_WAVES8) return first_tn_res<EPI1, F32, RES_WAVES8>(d1, v1, d2, v2, dry, st);
   if (v1.res == RES_SHARED) return first_tn_res<EPI1, F32, RES_SHARED>(d1, v1, d2, v2, dry, st);
   return hipErrorNotSupported;
 }

@@ -15,21 +15,28 @@ enum GemmLayout : int {
 // DMA two K steps to land (two stages wait on it after one); two workgroups per
 // CU run one's MFMAs under the other's load waits and epilogue.  Either needs
 // the stages to fit the CU's 160 KB of LDS.
+// RES_WAVES8 keeps one workgroup per CU but of 8 waves (two per SIMD, each a
+// 128x64 sub-tile), so one wave's MFMAs cover the other's LDS reads and waits.
 enum Residency : int {
-  RES_TWO = 0,     // 2 stages, one workgroup per CU
-  RES_THREE = 1,   // 3 stages, one workgroup per CU
-  RES_SHARED = 2,  // 2 stages, two workgroups per CU
+  RES_TWO = 0,     // 2 stages, one 4-wave workgroup per CU
+  RES_THREE = 1,   // 3 stages, one 4-wave workgroup per CU
+  RES_SHARED = 2,  // 2 stages, two 4-wave workgroups per CU
+  RES_WAVES8 = 3,  // 2 stages, one 8-wave workgroup per CU
 };
 constexpr int res_stages(int res) { return res == RES_THREE ? 3 : 2; }
 constexpr int res_wgs(int res) { return res == RES_SHARED ? 2 : 1; }
+constexpr int res_waves(int res) { return res == RES_WAVES8 ? 8 : 4; }
+// columns of one wave's sub-tile (the waves form a 2 x waves/2 grid)
+constexpr int res_wave_cols(int bn, int res) { return bn / (res_waves(res) / 2); }
 constexpr bool res_fits(int bm, int bn, int res) {
   return res_stages(res) * res_wgs(res) * 128 * (bm + bn) <= 160 * 1024;
 }
 
 // One launchable bf16 kernel variant.  Built tiles (bm x bn, residency):
-// 256x256 and 256x192 with RES_TWO; 256x128, 128x256, 128x192 and 128x128 with
-// RES_THREE; 128x192 and 128x128 with RES_SHARED.  192 columns not for the dual
-// or CE-statistics epilogues.  vec = 16-byte loads are legal for every operand
+// 256x256 and 256x192 with RES_TWO; 256x256 with RES_WAVES8 (not the dual
+// epilogue); 256x128, 128x256, 128x192 and 128x128 with RES_THREE; 128x192 and
+// 128x128 with RES_SHARED.  192 columns not for the dual or CE-statistics
+// epilogues.  vec = 16-byte loads are legal for every operand
 // (aligned pointers, leading dimensions and extents multiple of 8); without it
 // a 128x128 element-wise kernel runs whatever the tile fields say.
 struct GemmVariant {
@@ -42,7 +49,7 @@ hipError_t tp_launch_gemm_bf16(const GemmDesc &d, const GemmVariant &v, hipStrea
 hipError_t tp_launch_splitk_reduce(const GemmDesc &d, bool out_f32, bool vec, hipStream_t st);
 
 // Two independent bf16 products in one launch (the second must not be split),
-// both with the same residency.  With dry = true nothing is launched: the
+// both with the same residency (RES_TWO, RES_SHARED or RES_WAVES8).  With dry = true nothing is launched: the
 // return value only says whether the pair of variants is built (hipSuccess) or
 // not (hipErrorNotSupported).
 hipError_t tp_launch_gemm_pair(const GemmDesc &d1, const GemmVariant &v1, const GemmDesc &d2,

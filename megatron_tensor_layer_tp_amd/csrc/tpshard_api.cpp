@@ -155,7 +155,8 @@ struct TileCost {
   double step, step_long, alone, fixed, first;
 };
 constexpr TileCost kTiles[] = {
-    {256, 256, RES_TWO, 1.58, 1.58, 1.58, 11.3, 1.2},     {256, 192, RES_TWO, 1.26, 1.26, 1.26, 10.0, 1.0},
+    {256, 256, RES_WAVES8, 1.53, 1.53, 1.53, 11.3, 1.2},  {256, 256, RES_TWO, 1.58, 1.58, 1.58, 11.3, 1.2},
+    {256, 192, RES_TWO, 1.26, 1.26, 1.26, 10.0, 1.0},
     {256, 128, RES_THREE, 0.91, 0.91, 0.91, 10.0, 0.5},   {128, 256, RES_THREE, 0.91, 0.91, 0.91, 10.0, 0.7},
     {128, 192, RES_THREE, 0.72, 0.72, 0.72, 7.8, 1.6},    {128, 128, RES_THREE, 0.57, 0.57, 0.57, 6.0, 0.3},
     {128, 192, RES_SHARED, 1.15, 1.60, 0.78, 5.4, 9.6},   {128, 128, RES_SHARED, 0.975, 1.35, 0.65, 3.2, 3.6},
@@ -179,6 +180,7 @@ double epi_cost(int epi, bool out_f32, int res) {
 
 bool variant_built(int bm, int bn, int res, bool dual, int epi) {
   if (bn == 192 && (dual || epi == EPI_CE_STATS)) return false;
+  if (res == RES_WAVES8 && dual) return false;
   for (const TileCost &t : kTiles)
     if (t.bm == bm && t.bn == bn && t.res == res) return true;
   return false;
@@ -243,7 +245,7 @@ double plan_us(const Spec &s, const Plan &p) {
   return kLaunchUs + tile_cost(p.bm, p.bn, p.res).first + rounds * d + reduce_us(s, p);
 }
 
-// TP_GEMM_VARIANT="BMxBN:two|three|shared" restricts every bf16 product that has
+// TP_GEMM_VARIANT="BMxBN:two|three|shared|waves8" restricts every bf16 product that has
 // that variant built (and 16-byte operands) to it, split counts still chosen by
 // the cost model; the parity tests use it to run each variant on the same sizes.
 struct ForcedVariant {
@@ -257,7 +259,8 @@ ForcedVariant forced_variant() {
   char r[16] = {0};
   if (std::sscanf(e, "%dx%d:%15s", &f.bm, &f.bn, r) != 3) return f;
   const std::string rs(r);
-  f.res = rs == "two" ? RES_TWO : rs == "three" ? RES_THREE : rs == "shared" ? RES_SHARED : -1;
+  f.res = rs == "two" ? RES_TWO : rs == "three" ? RES_THREE : rs == "shared" ? RES_SHARED
+         : rs == "waves8" ? RES_WAVES8 : -1;
   f.on = f.res >= 0;
   return f;
 }
@@ -648,8 +651,8 @@ LmCePlan lm_ce_plan(int64_t s, int64_t h, int64_t Vs) {
   L.g = spec_nn(s, Vs, h, EPI_CE_STATS);
   L.g.out_f32 = true;
   L.p = plan_bf16(L.g);
-  L.parts = 2 * L.p.tiles_n;
-  L.width = L.p.bn / 2;
+  L.width = res_wave_cols(L.p.bn, L.p.res);  // one part per wave column of a tile
+  L.parts = L.p.tiles_n * (L.p.bn / L.width);
   L.bytes = align256((size_t)s * 3 * L.parts * sizeof(float));
   return L;
 }

@@ -18,7 +18,7 @@ from test_gpu_mlp import integer_exact_case
 
 pytestmark = pytest.mark.gpu
 
-VARIANTS = ["256x256:two", "256x192:two", "256x128:three", "128x256:three", "128x192:three",
+VARIANTS = ["256x256:two", "256x256:waves8", "256x192:two", "256x128:three", "128x256:three", "128x192:three",
             "128x128:three", "128x192:shared", "128x128:shared"]
 
 
