@@ -14,7 +14,7 @@ hipError_t launch_dma(const GemmDesc &d, hipStream_t st) {
 }
 
 // The built (tile, residency) variants: 256x256 and 256x192 with two stages;
-// 256x256 with 8 waves (not the dual epilogue); 256x128, 128x256, 128x192 and
+// 256x256 with 8 waves; 256x128, 128x256, 128x192 and
 // 128x128 with three; 128x192 and 128x128 also two workgroups per CU.
 // 192-column tiles not for the dual or CE epilogues.
 template <bool A_KC, bool B_KC, int EPI, bool OUT_F32, bool KSEG>
@@ -34,8 +34,7 @@ hipError_t launch_shape_k(const GemmDesc &d, int bm, int bn, int res, hipStream_
       if (bm == 256 && bn == 192) return launch_dma<256, 192, A_KC, B_KC, EPI, OUT_F32, KSEG, RES_TWO>(d, st);
     break;
   case RES_WAVES8:
-    if constexpr (EPI != EPI_SWIGLU_FWD)
-      if (bm == 256 && bn == 256) return launch_dma<256, 256, A_KC, B_KC, EPI, OUT_F32, KSEG, RES_WAVES8>(d, st);
+    if (bm == 256 && bn == 256) return launch_dma<256, 256, A_KC, B_KC, EPI, OUT_F32, KSEG, RES_WAVES8>(d, st);
     break;
   case RES_THREE:
     if (bm == 256 && bn == 128) return launch_dma<256, 128, A_KC, B_KC, EPI, OUT_F32, KSEG, RES_THREE>(d, st);

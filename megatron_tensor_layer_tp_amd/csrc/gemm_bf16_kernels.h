@@ -392,7 +392,7 @@ __device__ __forceinline__ void epilogue(const GemmDesc &d, f32x16 (&acc)[BM / 6
   static_assert(EPI != EPI_CE_STATS || (64 % LPR == 0 && 32 % RPI == 0), "CE rows span a DPP row");
   const int ci = lane & 31;
   const int rsub = 4 * (lane >> 5);
-  const int col_base = n0 + (DUAL ? wn * (BN / 4) : wn * WTN);
+  const int col_base = n0 + (DUAL ? wn * (BN / NW) : wn * WTN);  // DUAL: BN/NW gate + as many up columns
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
     __syncthreads();
@@ -644,10 +644,10 @@ __device__ __forceinline__ void lds_barrier() {
 
 // One operand tile (R rows of 64 k, or 64 k-rows of R columns) staged by
 // R/(8 NW) one-kilobyte DMA instructions per wave (NW waves).  DUAL: the R columns are two
-// sub-tiles of R/2 from two matrices; waves 0-1 fill the first, 2-3 the second.
+// sub-tiles of R/2 from two matrices; the first half of the waves fills the first, the
+// second half the second.
 template <int R, bool KC, bool DUAL, int NW = 4>
 struct Dma {
-  static_assert(!DUAL || NW == 4, "the dual operand is staged by 4 waves");
   static constexpr int NI = R / (8 * NW);  // kilobytes per wave
   static constexpr int REFF = DUAL ? R / 2 : R;   // columns of one row-contiguous sub-tile
   static constexpr int P = 2 * REFF;              // its k-row pitch (bytes)
@@ -773,7 +773,7 @@ __device__ __forceinline__ void dma_body(const GemmDesc &d, int lid, char *smem0
     const int ia = KSEG ? ks : 0, ib = KSEG ? ks : sn;
     Ab = (const uint16_t *)d.A[ia];
     lda = d.lda[ia];
-    Bb = (const uint16_t *)(DUAL ? d.B[wid >> 1] : d.B[ib]);
+    Bb = (const uint16_t *)(DUAL ? d.B[wid / (NW / 2)] : d.B[ib]);
     ldb = d.ldb[ib];
     klen = KSEG ? d.seg_len[ks] : d.K;
     da.init(lda, d.M - m0, wid, lane);
@@ -824,7 +824,7 @@ __device__ __forceinline__ void dma_body(const GemmDesc &d, int lid, char *smem0
     for (int h = 0; h < 2; ++h) {
       if constexpr (DUAL)
         brc[fn][h] = 128 * BM + (fn < FN / 2 ? 0 : 64 * BN) +
-                     rc_frag_off(BN, BN / 16, wn * (BN / 4) + (fn % (FN / 2)) * 32, h, lane);
+                     rc_frag_off(BN, BN / 16, wn * (BN / NW) + (fn % (FN / 2)) * 32, h, lane);
       else
         brc[fn][h] = 128 * BM + rc_frag_off(2 * BN, BN / 8, wn * WTN + fn * 32, h, lane);
     }

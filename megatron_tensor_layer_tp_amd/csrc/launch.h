@@ -33,8 +33,7 @@ constexpr bool res_fits(int bm, int bn, int res) {
 }
 
 // One launchable bf16 kernel variant.  Built tiles (bm x bn, residency):
-// 256x256 and 256x192 with RES_TWO; 256x256 with RES_WAVES8 (not the dual
-// epilogue); 256x128, 128x256, 128x192 and 128x128 with RES_THREE; 128x192 and
+// 256x256 and 256x192 with RES_TWO; 256x256 with RES_WAVES8; 256x128, 128x256, 128x192 and 128x128 with RES_THREE; 128x192 and
 // 128x128 with RES_SHARED.  192 columns not for the dual or CE-statistics
 // epilogues.  vec = 16-byte loads are legal for every operand
 // (aligned pointers, leading dimensions and extents multiple of 8); without it

@@ -180,7 +180,6 @@ double epi_cost(int epi, bool out_f32, int res) {
 
 bool variant_built(int bm, int bn, int res, bool dual, int epi) {
   if (bn == 192 && (dual || epi == EPI_CE_STATS)) return false;
-  if (res == RES_WAVES8 && dual) return false;
   for (const TileCost &t : kTiles)
     if (t.bm == bm && t.bn == bn && t.res == res) return true;
   return false;
