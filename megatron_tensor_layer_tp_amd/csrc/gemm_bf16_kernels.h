@@ -933,61 +933,15 @@ __device__ __forceinline__ void dma_body(const GemmDesc &d, int lid, char *smem0
   epilogue<BM, BN, EPI, OUT_F32, true, DUAL, NW>(d, acc, ep, lane, wm, wn, m0, n0, nlen, KSEG ? 0 : sn, split);
 }
 
-template <int BM_, int BN_, bool A_KC_, bool B_KC_, int EPI_, bool OUT_F32_, bool KSEG_>
-struct Cfg {
-  static constexpr int STAGE = 128 * (BM_ + BN_);
-  template <int NS, int NW>
-  static __device__ __forceinline__ void run(const GemmDesc &d, int lid, char *s0, char *s1, char *s2) {
-    dma_body<BM_, BN_, A_KC_, B_KC_, EPI_, OUT_F32_, KSEG_, NW, NS>(d, lid, s0, s1, s2);
-  }
-};
-
-// waves per SIMD of a residency (4 SIMDs per CU)
-constexpr int res_wpe(int res) { return res_wgs(res) * res_waves(res) / 4; }
-
-template <int BM, int BN, bool A_KC, bool B_KC, int EPI, bool OUT_F32, bool KSEG, int RES>
-__global__ void __launch_bounds__(64 * res_waves(RES))
-__attribute__((amdgpu_waves_per_eu(res_wpe(RES), res_wpe(RES)))) gemm_dma_kernel(GemmDesc d) {
-  static_assert(res_fits(BM, BN, RES), "LDS stages exceed the CU's 160 KB");
-  constexpr int S = 128 * (BM + BN), NS = res_stages(RES);
-  __shared__ __attribute__((aligned(1024))) char smem[NS * S];
-  dma_body<BM, BN, A_KC, B_KC, EPI, OUT_F32, KSEG, res_waves(RES), NS>(
-      d, xcd_lid(blockIdx.x, gridDim.x), smem, smem + S, NS == 3 ? smem + 2 * S : nullptr);
-}
-
-// Two independent products in one launch: workgroups [0, n1) compute the
-// first, the rest the second.  The first is the one with the longer tiles (a
-// long-K weight gradient), so its workgroups are dispatched first and the short
-// tiles of the second fill the CUs around them.  Each range gets the XCD remap
-// when n1 is a multiple of 8 (then both ranges start on XCD 0).
-template <class C1, class C2, int RES>
-__global__ void __launch_bounds__(64 * res_waves(RES))
-__attribute__((amdgpu_waves_per_eu(res_wpe(RES), res_wpe(RES)))) gemm_dma_pair_kernel(GemmDesc d1, GemmDesc d2,
-                                                                                      int n1, int n2) {
-  constexpr int S = C1::STAGE > C2::STAGE ? C1::STAGE : C2::STAGE, NS = res_stages(RES);
-  static_assert(NS * res_wgs(RES) * S <= 160 * 1024, "LDS stages exceed the CU's 160 KB");
-  __shared__ __attribute__((aligned(1024))) char smem[NS * S];
-  char *s2 = NS == 3 ? smem + 2 * S : nullptr;
-  const int b = blockIdx.x;
-  const bool remap = (n1 & 7) == 0;
-  if (b < n1) {
-    C1::template run<NS, res_waves(RES)>(d1, remap ? xcd_lid(b, n1) : b, smem, smem + S, s2);
-  } else {
-    const int r = b - n1;
-    C2::template run<NS, res_waves(RES)>(d2, remap ? xcd_lid(r, n2) : r, smem, smem + S, s2);
-  }
-}
-
 // Sum the split-K partials in split order (deterministic) and store.  Each
 // thread owns a run of 8 columns of one row (VEC: N and the segment widths
 // are multiples of 8); the scalar build owns single elements.
 template <bool OUT_F32, bool VEC>
-__global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmDesc d) {
+__device__ __forceinline__ void splitk_reduce_body(const GemmDesc &d, int64_t first, int64_t stride) {
   constexpr int W = VEC ? 8 : 1;
   const int runs = d.N / W;
   const int64_t total = (int64_t)d.M * runs;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
+  for (int64_t i = first; i < total; i += stride) {
     const int gm = (int)(i / runs);
     const int gc = (int)(i - (int64_t)gm * runs) * W;
     float s[W];
@@ -1024,4 +978,64 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmDesc d) {
   }
 }
 
+template <bool OUT_F32, bool VEC>
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmDesc d) {
+  splitk_reduce_body<OUT_F32, VEC>(d, (int64_t)blockIdx.x * blockDim.x + threadIdx.x,
+                                   (int64_t)gridDim.x * blockDim.x);
+}
+
 }  // namespace
+
+template <int BM_, int BN_, bool A_KC_, bool B_KC_, int EPI_, bool OUT_F32_, bool KSEG_>
+struct Cfg {
+  static constexpr int STAGE = 128 * (BM_ + BN_);
+  template <int NS, int NW>
+  static __device__ __forceinline__ void run(const GemmDesc &d, int lid, char *s0, char *s1, char *s2) {
+    dma_body<BM_, BN_, A_KC_, B_KC_, EPI_, OUT_F32_, KSEG_, NW, NS>(d, lid, s0, s1, s2);
+  }
+};
+
+// waves per SIMD of a residency (4 SIMDs per CU)
+constexpr int res_wpe(int res) { return res_wgs(res) * res_waves(res) / 4; }
+
+template <int BM, int BN, bool A_KC, bool B_KC, int EPI, bool OUT_F32, bool KSEG, int RES>
+__global__ void __launch_bounds__(64 * res_waves(RES))
+__attribute__((amdgpu_waves_per_eu(res_wpe(RES), res_wpe(RES)))) gemm_dma_kernel(GemmDesc d) {
+  static_assert(res_fits(BM, BN, RES), "LDS stages exceed the CU's 160 KB");
+  constexpr int S = 128 * (BM + BN), NS = res_stages(RES);
+  __shared__ __attribute__((aligned(1024))) char smem[NS * S];
+  dma_body<BM, BN, A_KC, B_KC, EPI, OUT_F32, KSEG, res_waves(RES), NS>(
+      d, xcd_lid(blockIdx.x, gridDim.x), smem, smem + S, NS == 3 ? smem + 2 * S : nullptr);
+}
+
+// Two independent products in one launch: workgroups [0, n1) compute the
+// first, [n1, n1 + n2) the second.  The first is the one with the longer tiles
+// (a long-K weight gradient), so its workgroups are dispatched first and the
+// short tiles of the second fill the CUs around them.  Each range gets the XCD
+// remap when n1 is a multiple of 8 (then both ranges start on XCD 0).  The last
+// n3 workgroups sum the split-K partials of an earlier launch's product (d3,
+// bf16 output, 16-byte runs): they are dispatched as the tiles drain.
+template <class C1, class C2, int RES>
+__global__ void __launch_bounds__(64 * res_waves(RES))
+__attribute__((amdgpu_waves_per_eu(res_wpe(RES), res_wpe(RES)))) gemm_dma_pair_kernel(GemmDesc d1, GemmDesc d2,
+                                                                                      int n1, int n2,
+                                                                                      GemmDesc d3, int n3) {
+  constexpr int S = C1::STAGE > C2::STAGE ? C1::STAGE : C2::STAGE, NS = res_stages(RES);
+  static_assert(NS * res_wgs(RES) * S <= 160 * 1024, "LDS stages exceed the CU's 160 KB");
+  __shared__ __attribute__((aligned(1024))) char smem[NS * S];
+  char *s2 = NS == 3 ? smem + 2 * S : nullptr;
+  const int b = blockIdx.x;
+  if (b >= n1 + n2) {
+    const int64_t nt = 64 * res_waves(RES);
+    splitk_reduce_body<false, true>(d3, (int64_t)(b - n1 - n2) * nt + threadIdx.x, (int64_t)n3 * nt);
+    return;
+  }
+  const bool remap = (n1 & 7) == 0;
+  if (b < n1) {
+    C1::template run<NS, res_waves(RES)>(d1, remap ? xcd_lid(b, n1) : b, smem, smem + S, s2);
+  } else {
+    const int r = b - n1;
+    C2::template run<NS, res_waves(RES)>(d2, remap ? xcd_lid(r, n2) : r, smem, smem + S, s2);
+  }
+}
+

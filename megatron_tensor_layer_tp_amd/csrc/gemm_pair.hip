@@ -16,45 +16,46 @@
 namespace {
 
 template <class C1, int RES>
-hipError_t second_nn(const GemmDesc &d1, const GemmDesc &d2, const GemmVariant &v2, bool dry, hipStream_t st) {
+hipError_t second_nn(const GemmDesc &d1, const GemmDesc &d2, const GemmVariant &v2, const GemmDesc *red, bool dry,
+                     hipStream_t st) {
   constexpr int BM = pair_bm(RES);
   if (v2.layout != GEMM_NN || v2.epi != EPI_STORE || v2.out_f32 || d2.kseg || v2.bm != BM || v2.res != RES)
     return hipErrorNotSupported;
   if (v2.bn == pair_wide(RES))
-    return go<C1, CfgL<BM, pair_wide(RES), GEMM_NN, EPI_STORE, false, false>, RES>(d1, d2, dry, st);
+    return go<C1, CfgL<BM, pair_wide(RES), GEMM_NN, EPI_STORE, false, false>, RES>(d1, d2, red, dry, st);
   if constexpr (pair_narrow(RES) != pair_wide(RES))
     if (v2.bn == pair_narrow(RES))
-      return go<C1, CfgL<BM, pair_narrow(RES), GEMM_NN, EPI_STORE, false, false>, RES>(d1, d2, dry, st);
+      return go<C1, CfgL<BM, pair_narrow(RES), GEMM_NN, EPI_STORE, false, false>, RES>(d1, d2, red, dry, st);
   return hipErrorNotSupported;
 }
 
 template <int RES>
-hipError_t first_nn(const GemmDesc &d1, const GemmVariant &v1, const GemmDesc &d2, const GemmVariant &v2, bool dry,
-                    hipStream_t st) {
+hipError_t first_nn(const GemmDesc &d1, const GemmVariant &v1, const GemmDesc &d2, const GemmVariant &v2,
+                    const GemmDesc *red, bool dry, hipStream_t st) {
   constexpr int BM = pair_bm(RES);
   if (v1.bm != BM) return hipErrorNotSupported;
   if (v1.bn == pair_wide(RES))
-    return second_nn<CfgL<BM, pair_wide(RES), GEMM_NN, EPI_STORE, false, false>, RES>(d1, d2, v2, dry, st);
+    return second_nn<CfgL<BM, pair_wide(RES), GEMM_NN, EPI_STORE, false, false>, RES>(d1, d2, v2, red, dry, st);
   if constexpr (pair_narrow(RES) != pair_wide(RES))
     if (v1.bn == pair_narrow(RES))
-      return second_nn<CfgL<BM, pair_narrow(RES), GEMM_NN, EPI_STORE, false, false>, RES>(d1, d2, v2, dry, st);
+      return second_nn<CfgL<BM, pair_narrow(RES), GEMM_NN, EPI_STORE, false, false>, RES>(d1, d2, v2, red, dry, st);
   return hipErrorNotSupported;
 }
 
 }  // namespace
 
 hipError_t tp_launch_gemm_pair(const GemmDesc &d1, const GemmVariant &v1, const GemmDesc &d2,
-                               const GemmVariant &v2, bool dry, hipStream_t st) {
+                               const GemmVariant &v2, const GemmDesc *red, bool dry, hipStream_t st) {
   if (!v1.vec || !v2.vec || d1.kseg || v1.res != v2.res) return hipErrorNotSupported;
   if (v1.layout == GEMM_TN) {
-    if (v1.epi == EPI_PARTIAL && v1.out_f32) return tp_launch_gemm_pair_tn_partial(d1, v1, d2, v2, dry, st);
-    if (v1.epi == EPI_STORE && !v1.out_f32) return first_tn<EPI_STORE, false>(d1, v1, d2, v2, dry, st);
+    if (v1.epi == EPI_PARTIAL && v1.out_f32) return tp_launch_gemm_pair_tn_partial(d1, v1, d2, v2, red, dry, st);
+    if (v1.epi == EPI_STORE && !v1.out_f32) return first_tn<EPI_STORE, false>(d1, v1, d2, v2, red, dry, st);
     return hipErrorNotSupported;
   }
   if (v1.layout == GEMM_NN && v1.epi == EPI_STORE && !v1.out_f32) {
-    if (v1.res == RES_TWO) return first_nn<RES_TWO>(d1, v1, d2, v2, dry, st);
-    if (v1.res == RES_WAVES8) return first_nn<RES_WAVES8>(d1, v1, d2, v2, dry, st);
-    if (v1.res == RES_SHARED) return first_nn<RES_SHARED>(d1, v1, d2, v2, dry, st);
+    if (v1.res == RES_TWO) return first_nn<RES_TWO>(d1, v1, d2, v2, red, dry, st);
+    if (v1.res == RES_WAVES8) return first_nn<RES_WAVES8>(d1, v1, d2, v2, red, dry, st);
+    if (v1.res == RES_SHARED) return first_nn<RES_SHARED>(d1, v1, d2, v2, red, dry, st);
   }
   return hipErrorNotSupported;
 }

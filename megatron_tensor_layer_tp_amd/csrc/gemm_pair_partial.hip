@@ -4,6 +4,6 @@
 #include "gemm_pair_impl.h"
 
 hipError_t tp_launch_gemm_pair_tn_partial(const GemmDesc &d1, const GemmVariant &v1, const GemmDesc &d2,
-                                          const GemmVariant &v2, bool dry, hipStream_t st) {
-  return first_tn<EPI_PARTIAL, true>(d1, v1, d2, v2, dry, st);
+                                          const GemmVariant &v2, const GemmDesc *red, bool dry, hipStream_t st) {
+  return first_tn<EPI_PARTIAL, true>(d1, v1, d2, v2, red, dry, st);
 }

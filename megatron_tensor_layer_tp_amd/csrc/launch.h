@@ -48,14 +48,17 @@ hipError_t tp_launch_gemm_bf16(const GemmDesc &d, const GemmVariant &v, hipStrea
 hipError_t tp_launch_splitk_reduce(const GemmDesc &d, bool out_f32, bool vec, hipStream_t st);
 
 // Two independent bf16 products in one launch (the second must not be split),
-// both with the same residency (RES_TWO, RES_SHARED or RES_WAVES8).  With dry = true nothing is launched: the
-// return value only says whether the pair of variants is built (hipSuccess) or
-// not (hipErrorNotSupported).
+// both with the same residency (RES_TWO, RES_SHARED or RES_WAVES8).  `red`
+// (may be null): the split-K reduction of an earlier launch's product (bf16
+// output, 16-byte runs, partials not written by this launch), run by extra
+// workgroups of this one.  With dry = true nothing is launched: the return
+// value only says whether the pair of variants is built (hipSuccess) or not
+// (hipErrorNotSupported).
 hipError_t tp_launch_gemm_pair(const GemmDesc &d1, const GemmVariant &v1, const GemmDesc &d2,
-                               const GemmVariant &v2, bool dry, hipStream_t st);
+                               const GemmVariant &v2, const GemmDesc *red, bool dry, hipStream_t st);
 // the pairs whose first product is a TN split-K partial (called by tp_launch_gemm_pair)
 hipError_t tp_launch_gemm_pair_tn_partial(const GemmDesc &d1, const GemmVariant &v1, const GemmDesc &d2,
-                                          const GemmVariant &v2, bool dry, hipStream_t st);
+                                          const GemmVariant &v2, const GemmDesc *red, bool dry, hipStream_t st);
 
 // fp32 storage and arithmetic (64x64 tiles, any layout, any extents).
 constexpr int TP_F32_TILE = 64;

@@ -466,7 +466,8 @@ PairPlan pair_plan(const Spec &s1, const Spec &s2, int dt) {
   for_each_plan(s1, [&](const Plan &p1) {
     for (const Plan &p2 : c2) {
       if (!p1.vec || !p2.vec || p1.res != p2.res) continue;
-      if (tp_launch_gemm_pair(d1, variant(s1, p1), d2, variant(b, p2), true, nullptr) != hipSuccess) continue;
+      if (tp_launch_gemm_pair(d1, variant(s1, p1), d2, variant(b, p2), nullptr, true, nullptr) != hipSuccess)
+        continue;
       const int64_t n1 = plan_blocks(p1), n2 = plan_blocks(p2);
       const double t = kLaunchUs +
                        std::max(tile_cost(p1.bm, p1.bn, p1.res).first, tile_cost(p2.bm, p2.bn, p2.res).first) +
@@ -488,18 +489,44 @@ size_t pair_ws_bytes(const Spec &s1, const Spec &s2, int dt) {
   return std::max(align256(pp.p1.ws_bytes), align256(pp.p2.ws_bytes));
 }
 
+// A split-K reduction left for the next paired launch of the same call to run
+// in extra workgroups (it must not write the partials this one reads).
+struct PendingReduce {
+  bool on = false;
+  GemmDesc d;
+};
+
+// Run two independent products (paired when planned so).  `in` (may be null):
+// a pending reduction of an earlier pair, run here first (inside the pair
+// launch when there is one).  `out` (may be null): receives this pair's own
+// split-K reduction instead of launching it, when it can run inside a later
+// pair (bf16 output, 16-byte runs).
 int run_pair(const Spec &s1, const Ptrs &q1, const Spec &s2, const Ptrs &q2, int dt, void *ws, hipStream_t st,
-             const char *what1, const char *what2) {
+             const char *what1, const char *what2, PendingReduce *in = nullptr, PendingReduce *out = nullptr) {
   const PairPlan pp = pair_plan(s1, s2, dt);
+  const GemmDesc *red = (in != nullptr && in->on) ? &in->d : nullptr;
   if (!pp.paired) {
+    if (red != nullptr) {
+      if (hipError_t e = tp_launch_splitk_reduce(*red, false, true, st))
+        return fail(TP_EHIP, "%s: pending reduction: %s", what1, hipGetErrorString(e));
+      in->on = false;
+    }
     if (int e = run_planned(s1, pp.p1, q1, dt, ws, st, what1)) return e;
     return run_planned(s2, pp.p2, q2, dt, ws, st, what2);
   }
   if (pp.p1.splits > 1 && ws == nullptr) return fail(TP_EWORKSPACE, "%s: split-K plan without workspace", what1);
   const GemmDesc d1 = make_desc(s1, q1, pp.p1, dt, ws);
   const GemmDesc d2 = make_desc(s2, q2, pp.p2, dt, nullptr);
-  hipError_t e = tp_launch_gemm_pair(d1, variant(s1, pp.p1), d2, variant(s2, pp.p2), false, st);
-  if (e == hipSuccess && pp.p1.splits > 1) e = tp_launch_splitk_reduce(d1, s1.out_f32, pp.p1.vec, st);
+  hipError_t e = tp_launch_gemm_pair(d1, variant(s1, pp.p1), d2, variant(s2, pp.p2), red, false, st);
+  if (red != nullptr) in->on = false;
+  if (e == hipSuccess && pp.p1.splits > 1) {
+    if (out != nullptr && !s1.out_f32 && pp.p1.vec) {
+      out->on = true;
+      out->d = d1;
+    } else {
+      e = tp_launch_splitk_reduce(d1, s1.out_f32, pp.p1.vec, st);
+    }
+  }
   if (e != hipSuccess) return fail(TP_EHIP, "%s + %s: %s", what1, what2, hipGetErrorString(e));
   return TP_OK;
 }
@@ -541,7 +568,7 @@ Spec spec_tn(int64_t M, int64_t N, int64_t K) {
 // tp_mlp_bwd workspace: dZ [s,ft] then the split-K partials of dW1 / dW2
 struct MlpBwdLayout {
   Spec g_dz, g_dw2, g_dx, g_dw1;
-  size_t dz_bytes = 0, part_bytes = 0, total = 0;
+  size_t dz_bytes = 0, part1_bytes = 0, part2_bytes = 0, total = 0;
 };
 MlpBwdLayout mlp_bwd_layout(int dt, int64_t s, int64_t h, int64_t ft) {
   MlpBwdLayout L;
@@ -552,14 +579,16 @@ MlpBwdLayout mlp_bwd_layout(int dt, int64_t s, int64_t h, int64_t ft) {
   L.g_dw1 = spec_tn(h, ft, s);
   for (Spec *g : {&L.g_dz, &L.g_dw2, &L.g_dx, &L.g_dw1}) g->can_split = true;
   L.dz_bytes = align256((size_t)s * ft * esize(dt));
-  L.part_bytes = std::max(pair_ws_bytes(L.g_dw2, L.g_dz, dt), pair_ws_bytes(L.g_dw1, L.g_dx, dt));
-  L.total = L.dz_bytes + L.part_bytes;
+  // the two passes' split-K partials apart: the second pass runs the first's reduction
+  L.part1_bytes = align256(pair_ws_bytes(L.g_dw2, L.g_dz, dt));
+  L.part2_bytes = align256(pair_ws_bytes(L.g_dw1, L.g_dx, dt));
+  L.total = L.dz_bytes + L.part1_bytes + L.part2_bytes;
   return L;
 }
 
 struct SwigluBwdLayout {
   Spec g_da, g_dwd, g_dx, g_dwgu;
-  size_t dg_bytes = 0, part_bytes = 0, total = 0;
+  size_t dg_bytes = 0, part1_bytes = 0, part2_bytes = 0, total = 0;
 };
 SwigluBwdLayout swiglu_bwd_layout(int dt, int64_t s, int64_t h, int64_t ft) {
   SwigluBwdLayout L;
@@ -592,14 +621,15 @@ SwigluBwdLayout swiglu_bwd_layout(int dt, int64_t s, int64_t h, int64_t ft) {
   L.g_dwgu = dw;
   for (Spec *g : {&L.g_da, &L.g_dwd, &L.g_dx, &L.g_dwgu}) g->can_split = true;
   L.dg_bytes = align256((size_t)s * ft * esize(dt));
-  L.part_bytes = std::max(pair_ws_bytes(L.g_dwd, L.g_da, dt), pair_ws_bytes(L.g_dwgu, L.g_dx, dt));
-  L.total = 2 * L.dg_bytes + L.part_bytes;
+  L.part1_bytes = align256(pair_ws_bytes(L.g_dwd, L.g_da, dt));
+  L.part2_bytes = align256(pair_ws_bytes(L.g_dwgu, L.g_dx, dt));
+  L.total = 2 * L.dg_bytes + L.part1_bytes + L.part2_bytes;
   return L;
 }
 
 struct AttnBwdLayout {
   Spec g_dx, g_dwqkv, g_do, g_dwo;
-  size_t part_bytes = 0, total = 0;
+  size_t part1_bytes = 0, part2_bytes = 0, total = 0;
 };
 AttnBwdLayout attn_bwd_layout(int dt, int64_t s, int64_t h, int64_t dq, int64_t dkv) {
   AttnBwdLayout L;
@@ -633,8 +663,9 @@ AttnBwdLayout attn_bwd_layout(int dt, int64_t s, int64_t h, int64_t dq, int64_t 
   L.g_do = spec_nt(s, dq, h, EPI_STORE);
   L.g_dwo = spec_tn(dq, h, s);
   for (Spec *g : {&L.g_dx, &L.g_dwqkv, &L.g_do, &L.g_dwo}) g->can_split = true;
-  L.part_bytes = std::max(pair_ws_bytes(L.g_dwqkv, L.g_dx, dt), pair_ws_bytes(L.g_dwo, L.g_do, dt));
-  L.total = L.part_bytes;
+  L.part1_bytes = align256(pair_ws_bytes(L.g_dwqkv, L.g_dx, dt));
+  L.part2_bytes = align256(pair_ws_bytes(L.g_dwo, L.g_do, dt));
+  L.total = L.part1_bytes + L.part2_bytes;
   return L;
 }
 
@@ -752,7 +783,8 @@ int tp_mlp_bwd(int act, int dt, int64_t s, int64_t h, int64_t ft, const void *X,
   hipStream_t st = (hipStream_t)stream;
   char *wsb = (char *)ws;
   void *dZ = wsb;
-  void *part = wsb + L.dz_bytes;
+  void *part1 = wsb + L.dz_bytes, *part2 = wsb + L.dz_bytes + L.part1_bytes;
+  PendingReduce pend;
   const int a = act == TP_ACT_GELU ? ACT_GELU : ACT_RELU;
   {  // dW2 = H^T . dY  beside  dZ = (dY . W2^T) * act'(Z)  (ReLU mask from Z, or from H without Z)
     Ptrs pw;
@@ -765,7 +797,8 @@ int tp_mlp_bwd(int act, int dt, int64_t s, int64_t h, int64_t ft, const void *X,
     pz.C[0] = dZ; pz.ldc[0] = ft;
     pz.ai0 = Z ? Z : H; pz.ldai = ft;
     pz.act = a;
-    if (int e = run_pair(L.g_dw2, pw, L.g_dz, pz, dt, part, st, "tp_mlp_bwd dW2 GEMM", "tp_mlp_bwd dZ GEMM"))
+    if (int e = run_pair(L.g_dw2, pw, L.g_dz, pz, dt, part1, st, "tp_mlp_bwd dW2 GEMM", "tp_mlp_bwd dZ GEMM",
+                         nullptr, &pend))
       return e;
   }
   {  // dW1 = X^T . dZ  beside  dX = dZ . W1^T
@@ -777,7 +810,8 @@ int tp_mlp_bwd(int act, int dt, int64_t s, int64_t h, int64_t ft, const void *X,
     px.A[0] = dZ; px.lda[0] = ft;
     px.B[0] = W1; px.ldb[0] = ft;
     px.C[0] = dX; px.ldc[0] = h;
-    if (int e = run_pair(L.g_dw1, pw, L.g_dx, px, dt, part, st, "tp_mlp_bwd dW1 GEMM", "tp_mlp_bwd dX GEMM"))
+    if (int e = run_pair(L.g_dw1, pw, L.g_dx, px, dt, part2, st, "tp_mlp_bwd dW1 GEMM", "tp_mlp_bwd dX GEMM",
+                         &pend))
       return e;
   }
   return ok();
@@ -841,7 +875,9 @@ int tp_swiglu_bwd(int dt, int64_t s, int64_t h, int64_t ft, const void *X, const
   if (c.status) return c.status;
   hipStream_t st = (hipStream_t)stream;
   char *wsb = (char *)ws;
-  void *dG = wsb, *dU = wsb + L.dg_bytes, *part = wsb + 2 * L.dg_bytes;
+  void *dG = wsb, *dU = wsb + L.dg_bytes, *part1 = wsb + 2 * L.dg_bytes;
+  void *part2 = (char *)part1 + L.part1_bytes;
+  PendingReduce pend;
   {  // dWd = A^T . dY  beside  dA = dY . Wd^T, dG = dA * U * SiLU'(G), dU = dA * SiLU(G)
     Ptrs pw;
     pw.A[0] = A; pw.lda[0] = ft;
@@ -853,7 +889,8 @@ int tp_swiglu_bwd(int dt, int64_t s, int64_t h, int64_t ft, const void *X, const
     pa.C[0] = dG; pa.ldc[0] = ft;
     pa.ai0 = G; pa.ai1 = U; pa.ldai = ft;
     pa.ao0 = dU; pa.ldao = ft;
-    if (int e = run_pair(L.g_dwd, pw, L.g_da, pa, dt, part, st, "tp_swiglu_bwd dWd GEMM", "tp_swiglu_bwd dA GEMM"))
+    if (int e = run_pair(L.g_dwd, pw, L.g_da, pa, dt, part1, st, "tp_swiglu_bwd dWd GEMM", "tp_swiglu_bwd dA GEMM",
+                         nullptr, &pend))
       return e;
   }
   {  // [dWg | dWu] = X^T . [dG | dU]  beside  dX = dG . Wg^T + dU . Wu^T
@@ -865,8 +902,8 @@ int tp_swiglu_bwd(int dt, int64_t s, int64_t h, int64_t ft, const void *X, const
     px.A[0] = dG; px.A[1] = dU; px.lda[0] = px.lda[1] = ft;
     px.B[0] = Wg; px.B[1] = Wu; px.ldb[0] = px.ldb[1] = ft;
     px.C[0] = dX; px.ldc[0] = h;
-    if (int e = run_pair(L.g_dwgu, pw, L.g_dx, px, dt, part, st, "tp_swiglu_bwd dWg/dWu GEMM",
-                         "tp_swiglu_bwd dX GEMM"))
+    if (int e = run_pair(L.g_dwgu, pw, L.g_dx, px, dt, part2, st, "tp_swiglu_bwd dWg/dWu GEMM",
+                         "tp_swiglu_bwd dX GEMM", &pend))
       return e;
   }
   return ok();
@@ -943,6 +980,8 @@ int tp_attn_proj_bwd(int dt, int64_t s, int64_t h, int64_t dq, int64_t dkv, cons
   ws_ok(c, ws, ws_bytes, L.total, "tp_attn_proj_bwd");
   if (c.status) return c.status;
   hipStream_t st = (hipStream_t)stream;
+  void *part1 = ws, *part2 = (char *)ws + L.part1_bytes;
+  PendingReduce pend;
   {  // [dWq | dWk | dWv] = X^T . [dQ | dK | dV]  beside  dX = dQ.Wq^T + dK.Wk^T + dV.Wv^T (K-segments)
     Ptrs pw;
     pw.A[0] = X; pw.lda[0] = h;
@@ -956,8 +995,8 @@ int tp_attn_proj_bwd(int dt, int64_t s, int64_t h, int64_t dq, int64_t dkv, cons
     px.B[0] = Wq; px.B[1] = Wk; px.B[2] = Wv;
     px.ldb[0] = dq; px.ldb[1] = px.ldb[2] = dkv;
     px.C[0] = dX; px.ldc[0] = h;
-    if (int e = run_pair(L.g_dwqkv, pw, L.g_dx, px, dt, ws, st, "tp_attn_proj_bwd dWqkv GEMM",
-                         "tp_attn_proj_bwd dX GEMM"))
+    if (int e = run_pair(L.g_dwqkv, pw, L.g_dx, px, dt, part1, st, "tp_attn_proj_bwd dWqkv GEMM",
+                         "tp_attn_proj_bwd dX GEMM", nullptr, &pend))
       return e;
   }
   {  // dWo = O^T . dY  beside  dO = dY . Wo^T
@@ -969,7 +1008,8 @@ int tp_attn_proj_bwd(int dt, int64_t s, int64_t h, int64_t dq, int64_t dkv, cons
     po.A[0] = dY; po.lda[0] = h;
     po.B[0] = Wo; po.ldb[0] = h;
     po.C[0] = dO; po.ldc[0] = dq;
-    if (int e = run_pair(L.g_dwo, pw, L.g_do, po, dt, ws, st, "tp_attn_proj_bwd dWo GEMM", "tp_attn_proj_bwd dO GEMM"))
+    if (int e = run_pair(L.g_dwo, pw, L.g_do, po, dt, part2, st, "tp_attn_proj_bwd dWo GEMM",
+                         "tp_attn_proj_bwd dO GEMM", &pend))
       return e;
   }
   return ok();
