@@ -377,11 +377,11 @@ def traffic_for(kernel_key: str):
 # algorithmic bytes per launch at the V=128256 t=8 vocab shard, s = h = 8192).
 _S5, _H5, _V5 = 8192, 8192, 16032
 TRAFFIC_KERNELS = {
-    "lm_head_gemm": ("lm", "gemm_dma_kernel<256, 256, true, false, 0, true, false>",
-                     ["gemm_bf16_kernels.h", "gemm_bf16.hip", "gemm_desc.h"],
+    "lm_head_gemm": ("lm", "gemm_dma_kernel<256, 256, true, false, 0, true, false, 3>",
+                     ["gemm_bf16_kernels.h", "gemm_bf16.hip", "gemm_desc.h", "launch.h"],
                      2 * _S5 * _H5 + 2 * _H5 * _V5 + 4 * _S5 * _V5),
-    "lm_head_ce_gemm": ("lmce", "gemm_dma_kernel<256, 256, true, false, 6, true, false>",
-                        ["gemm_bf16_kernels.h", "gemm_bf16.hip", "gemm_desc.h"],
+    "lm_head_ce_gemm": ("lmce", "gemm_dma_kernel<256, 256, true, false, 6, true, false, 3>",
+                        ["gemm_bf16_kernels.h", "gemm_bf16.hip", "gemm_desc.h", "launch.h"],
                         2 * _S5 * _H5 + 2 * _H5 * _V5 + 8 * _S5),
     "vocab_ce": ("ce", "vocab_ce_kernel<4>", ["vocab.hip"], 4 * _S5 * _V5 + 8 * _S5 + 12 * _S5),
     "vocab_ce_bwd": ("cebwd", "vocab_ce_bwd_kernel<4, true>", ["vocab.hip"],
@@ -530,7 +530,7 @@ def main():
     if "lm_head_fwd" in by:
         r = by["lm_head_fwd"]
         ach = r.flops / (r.ms() * 1e-3) / 1e12
-        res["roofline"] = {"kernel": "gemm_dma_kernel<256,256,NN,store fp32> (tp_lm_head_fwd)",
+        res["roofline"] = {"kernel": "gemm_dma_kernel<256,256,NN,store fp32,8 waves> (tp_lm_head_fwd)",
                            "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
                            "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
                            "traffic": traffic_for("lm_head_gemm")}
