@@ -35,6 +35,7 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BK = 64;
 constexpr int NTHREADS = 256;
@@ -224,10 +225,14 @@ __device__ __forceinline__ void epi8(const GemmDesc &d, int gm, int gn, int nlen
       for (int q = 0; q < cnt; ++q) o[q] = x[q];
     }
   } else if constexpr (EPI == EPI_STORE && OUT_F32) {
+    // fp32 outputs (the LM head's logits) are streamed past the caches: they are read
+    // back only by a later kernel, and dirty lines left in the Infinity Cache would be
+    // written back while that kernel streams them in
     float *o = (float *)d.C[sc] + (int64_t)gm * d.ldc[sc] + gn;
     if (full) {
-      *(float4 *)o = make_float4(x[0], x[1], x[2], x[3]);
-      *(float4 *)(o + 4) = make_float4(x[4], x[5], x[6], x[7]);
+      const f32x4 lo = {x[0], x[1], x[2], x[3]}, hi = {x[4], x[5], x[6], x[7]};
+      __builtin_nontemporal_store(lo, (f32x4 *)o);
+      __builtin_nontemporal_store(hi, (f32x4 *)(o + 4));
     } else {
       for (int q = 0; q < cnt; ++q) o[q] = x[q];
     }
