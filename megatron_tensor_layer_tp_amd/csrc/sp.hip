@@ -120,6 +120,44 @@ __device__ __forceinline__ void store8(uint16_t *row, int i, int h, const float 
   }
 }
 
+// the same 8 elements kept packed until used (4 registers instead of 8): bf16 bits and mask bytes
+template <bool VEC>
+__device__ __forceinline__ u32x4 raw8(const uint16_t *row, int i, int h) {
+  u32x4 w = {0u, 0u, 0u, 0u};
+  if constexpr (VEC) {
+    const int c = col_of<true>(i, 0);
+    if (c < h) w = *(const u32x4 *)(row + c);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int c = col_of<false>(i, q);
+      if (c < h) w[q >> 1] |= (uint32_t)row[c] << (16 * (q & 1));
+    }
+  }
+  return w;
+}
+template <bool VEC>
+__device__ __forceinline__ uint2 rawmask8(const uint8_t *row, int i, int h) {
+  uint2 m = make_uint2(0u, 0u);
+  if constexpr (VEC) {
+    const int c = col_of<true>(i, 0);
+    if (c < h) m = *(const uint2 *)(row + c);
+  } else {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int c = col_of<false>(i, q);
+      if (c < h) {
+        if (q < 4) m.x |= (uint32_t)row[c] << (8 * q);
+        else m.y |= (uint32_t)row[c] << (8 * (q - 4));
+      }
+    }
+  }
+  return m;
+}
+__device__ __forceinline__ float mask_at(const uint2 &m, int q) {
+  return (float)(((q < 4 ? m.x : m.y) >> (8 * (q & 3))) & 0xffu);
+}
+
 struct SpArgs {
   int64_t n, h;
   float keep, eps;  // 1 / (1 - p), LayerNorm epsilon
@@ -166,7 +204,8 @@ __global__ void __launch_bounds__(SP_THREADS) sp_ln_fwd_kernel(SpArgs a) {
     uint16_t *ur = a.uo + r * a.h, *zr = a.z + r * a.h;
 #pragma unroll
     for (int i = 0; i < NP * SP_VPT; ++i) {
-      float gv[8], bv[8], zv[8];
+      // gamma and beta are shared by every row: L2 hits
+      float zv[8], gv[8], bv[8];
       load8<VEC>(a.gamma, i, h, gv);
       load8<VEC>(a.beta, i, h, bv);
 #pragma unroll
@@ -187,7 +226,10 @@ __global__ void __launch_bounds__(SP_THREADS) sp_ln_bwd_kernel(SpArgs a) {
   const int h = (int)a.h;
   for (int64_t r = blockIdx.x; r < a.n; r += gridDim.x) {
     const float mean = a.mean[r], rstd = a.rstd[r];
+    // every load of the row is issued before the first reduction
     float xh[NP * SP_VPT][8], g[NP * SP_VPT][8];
+    u32x4 dnw[NP * SP_VPT];
+    uint2 mw[NP * SP_VPT];
     float sg = 0.f, sgx = 0.f;
 #pragma unroll
     for (int i = 0; i < NP * SP_VPT; ++i) {
@@ -195,6 +237,8 @@ __global__ void __launch_bounds__(SP_THREADS) sp_ln_bwd_kernel(SpArgs a) {
       load8<VEC>(a.u + r * a.h, i, h, uv);
       load8<VEC>(a.dz + r * a.h, i, h, dzv);
       load8<VEC>(a.gamma, i, h, gv);
+      dnw[i] = raw8<VEC>(a.dun + r * a.h, i, h);
+      mw[i] = rawmask8<VEC>(a.mask + r * a.h, i, h);
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const bool in = col_of<VEC>(i, q) < h;
@@ -208,13 +252,12 @@ __global__ void __launch_bounds__(SP_THREADS) sp_ln_bwd_kernel(SpArgs a) {
     const float mgx = block_sum(sgx, red) / (float)h;
 #pragma unroll
     for (int i = 0; i < NP * SP_VPT; ++i) {
-      float dn[8], mv[8], dxv[8], dyv[8];
-      load8<VEC>(a.dun + r * a.h, i, h, dn);
-      mask8<VEC>(a.mask + r * a.h, i, h, mv);
+      float dxv[8], dyv[8], dn[8];
+      unpack8(dnw[i], dn);
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         dxv[q] = fmaf(rstd, g[i][q] - mg - xh[i][q] * mgx, dn[q]);
-        dyv[q] = dxv[q] * mv[q] * a.keep;
+        dyv[q] = dxv[q] * mask_at(mw[i], q) * a.keep;
       }
       store8<VEC>(a.dx + r * a.h, i, h, dxv);
       store8<VEC>(a.dy + r * a.h, i, h, dyv);
@@ -233,6 +276,27 @@ __global__ void __launch_bounds__(256) sp_ln_param_partial_kernel(SpArgs a) {
 #pragma unroll
   for (int q = 0; q < 8; ++q) pg[q] = pb[q] = 0.f;
   const bool full = c0 + 8 <= a.h && (a.h & 7) == 0;
+  if (full && r1 - r0 == SP_RCHUNK) {
+    // a whole chunk: all 2 x 16 loads in flight at once, then the fixed-order sums
+    u32x4 uw[SP_RCHUNK], dw[SP_RCHUNK];
+#pragma unroll
+    for (int j = 0; j < SP_RCHUNK; ++j) {
+      uw[j] = *(const u32x4 *)(a.u + (r0 + j) * a.h + c0);
+      dw[j] = *(const u32x4 *)(a.dz + (r0 + j) * a.h + c0);
+    }
+#pragma unroll
+    for (int j = 0; j < SP_RCHUNK; ++j) {
+      const float mean = a.mean[r0 + j], rstd = a.rstd[r0 + j];
+      float uv[8], dzv[8];
+      unpack8(uw[j], uv);
+      unpack8(dw[j], dzv);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        pg[q] = fmaf(dzv[q], (uv[q] - mean) * rstd, pg[q]);
+        pb[q] += dzv[q];
+      }
+    }
+  } else {
 #pragma unroll 4
   for (int64_t r = r0; r < r1; ++r) {
     const float mean = a.mean[r], rstd = a.rstd[r];
@@ -253,6 +317,7 @@ __global__ void __launch_bounds__(256) sp_ln_param_partial_kernel(SpArgs a) {
       pg[q] = fmaf(dzv[q], (uv[q] - mean) * rstd, pg[q]);
       pb[q] += dzv[q];
     }
+  }
   }
   float *pr = a.part + (int64_t)blockIdx.y * 2 * a.h;
 #pragma unroll
