@@ -212,7 +212,7 @@ __device__ __forceinline__ void unpack8(const u32x4 &w, float *v) {
 // accesses; a ragged tail (or the scalar build) goes element by element.
 template <int EPI, bool OUT_F32, bool VEC>
 __device__ __forceinline__ void epi8(const GemmDesc &d, int gm, int gn, int nlen, int sc, int split,
-                                     const float *x, const float *u) {
+                                     const float *x, const float *u, const u32x4 *pre = nullptr) {
   const int cnt = min(8, nlen - gn);
   const bool full = VEC && cnt == 8;
   if constexpr (EPI == EPI_PARTIAL) {
@@ -243,7 +243,10 @@ __device__ __forceinline__ void epi8(const GemmDesc &d, int gm, int gn, int nlen
     const bool has_ai = EPI == EPI_ACT_BWD || EPI == EPI_SWIGLU_BWD;
     if constexpr (has_ai) {
       const int64_t o = (int64_t)gm * d.ldai + gn;
-      if (full) {
+      if (full && pre != nullptr) {  // loaded ahead by the caller
+        unpack8(pre[0], a0);
+        if constexpr (EPI == EPI_SWIGLU_BWD) unpack8(pre[1], a1);
+      } else if (full) {
         unpack8(*(const u32x4 *)((const uint16_t *)d.ai0 + o), a0);
         if constexpr (EPI == EPI_SWIGLU_BWD) unpack8(*(const u32x4 *)((const uint16_t *)d.ai1 + o), a1);
       } else {
@@ -398,8 +401,35 @@ __device__ __forceinline__ void epilogue(const GemmDesc &d, f32x16 (&acc)[BM / 6
   const int ci = lane & 31;
   const int rsub = 4 * (lane >> 5);
   const int col_base = n0 + (DUAL ? wn * (BN / NW) : wn * WTN);  // DUAL: BN/NW gate + as many up columns
+  // epilogues that read inputs (Z, or G and U) issue this strip's loads before its
+  // LDS round trip, so their latency runs under the barriers and LDS writes
+  constexpr bool PRE = VEC && (EPI == EPI_ACT_BWD || EPI == EPI_SWIGLU_BWD);
+  constexpr int NPRE = PRE ? NIT : 1;
+  auto pass_at = [&](int fm, int it, int &gm, int &gn, bool &live, int &r, int &c) {
+    const int r0 = it * RPI + lane / LPR;
+    live = lane < RPI * LPR && r0 < 32;
+    r = live ? r0 : 0;
+    c = (lane % LPR) * 8;
+    gm = m0 + wm * WTM + fm * 32 + r;
+    gn = col_base + c;
+  };
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) {
+    u32x4 pre[NPRE][2];
+    if constexpr (PRE) {
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        int gm, gn, r, c;
+        bool live;
+        pass_at(fm, it, gm, gn, live, r, c);
+        pre[it][0] = pre[it][1] = u32x4{0u, 0u, 0u, 0u};
+        if (live && gm < d.M && gn + 8 <= nlen) {
+          const int64_t o = (int64_t)gm * d.ldai + gn;
+          pre[it][0] = *(const u32x4 *)((const uint16_t *)d.ai0 + o);
+          if constexpr (EPI == EPI_SWIGLU_BWD) pre[it][1] = *(const u32x4 *)((const uint16_t *)d.ai1 + o);
+        }
+      }
+    }
     __syncthreads();
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
@@ -407,7 +437,7 @@ __device__ __forceinline__ void epilogue(const GemmDesc &d, f32x16 (&acc)[BM / 6
       for (int e = 0; e < 16; ++e)
         ep[(8 * (e >> 2) + rsub + (e & 3)) * EPS + fn * 32 + ci] = acc[fm][fn][e];
     __syncthreads();
-#pragma unroll 2
+#pragma unroll PRE ? NIT : 2
     for (int it = 0; it < NIT; ++it) {
       const int r0 = it * RPI + lane / LPR;
       const bool live = lane < RPI * LPR && r0 < 32;
@@ -427,7 +457,8 @@ __device__ __forceinline__ void epilogue(const GemmDesc &d, f32x16 (&acc)[BM / 6
         // one part per wave column of every tile: BN / WTN parts per tile
         ce_stats8<LPR>(d, gm, gn, nlen, col_base / WTN, (BN / WTN) * d.tiles_n, lane, x);
       } else {
-        if (live && gm < d.M && gn < nlen) epi8<EPI, OUT_F32, VEC>(d, gm, gn, nlen, sc, split, x, u);
+        if (live && gm < d.M && gn < nlen)
+          epi8<EPI, OUT_F32, VEC>(d, gm, gn, nlen, sc, split, x, u, PRE ? pre[PRE ? it : 0] : nullptr);
       }
     }
   }
