@@ -387,6 +387,47 @@ __device__ __forceinline__ void ce_stats8(const GemmDesc &d, int gm, int gn, int
 // column l%32 of the block.  `ep` is this wave's private strip (32 x (WTN+8)).
 // All waves of the workgroup must call it (it holds workgroup barriers).
 // ---------------------------------------------------------------------------
+// fp32 outputs straight from the accumulator layout: a half-wave's 32 lanes hold
+// 32 consecutive columns of one row, so each 4-byte store instruction writes two
+// full 128-byte row segments; no LDS round trip and no workgroup barrier.  The
+// stored outputs (fp32 C, e.g. logits) stream past the caches, since a later
+// kernel reads them; split-K partials (PARTIAL) stay cacheable for the reduction.
+template <int BM, int BN, int NW, bool PARTIAL>
+__device__ __forceinline__ void epilogue_f32_direct(const GemmDesc &d, f32x16 (&acc)[BM / 64][2 * BN / NW / 32],
+                                                    int lane, int wm, int wn, int m0, int n0, int nlen, int sc,
+                                                    int split) {
+  constexpr int WTM = BM / 2, WTN = BN / (NW / 2), FM = WTM / 32, FN = WTN / 32;
+  float *C;
+  int64_t ldc;
+  int coff = 0;  // column of the tile's first output column in C
+  if constexpr (PARTIAL) {
+    C = d.ws + (int64_t)split * d.M * d.N;
+    ldc = d.N;
+    coff = d.kseg ? 0 : d.seg_col0[sc];
+  } else {
+    C = (float *)d.C[sc];
+    ldc = d.ldc[sc];
+  }
+  const int rsub = 4 * (lane >> 5);
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) {
+    const int gn = n0 + wn * WTN + fn * 32 + (lane & 31);
+    if (gn >= nlen) continue;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int r0 = m0 + wm * WTM + fm * 32 + rsub;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int gm = r0 + 8 * (e >> 2) + (e & 3);
+        if (gm >= d.M) continue;
+        float *o = C + (int64_t)gm * ldc + coff + gn;
+        if constexpr (PARTIAL) *o = acc[fm][fn][e];
+        else __builtin_nontemporal_store(acc[fm][fn][e], o);
+      }
+    }
+  }
+}
+
 template <int BM, int BN, int EPI, bool OUT_F32, bool VEC, bool DUAL, int NW = 4>
 __device__ __forceinline__ void epilogue(const GemmDesc &d, f32x16 (&acc)[BM / 64][2 * BN / NW / 32], float *ep,
                                          int lane, int wm, int wn, int m0, int n0, int nlen, int sc, int split) {
@@ -966,6 +1007,10 @@ __device__ __forceinline__ void dma_body(const GemmDesc &d, int lid, char *smem0
   // epilogue strips: the first half of the waves in stage 0, the rest in stage 1 (the first
   // __syncthreads inside the epilogue retires the last tile)
   float *ep = (float *)(wid < NW / 2 ? smem0 : smem1) + (wid % (NW / 2)) * 32 * (WTN + 8);
+  if constexpr ((EPI == EPI_STORE && OUT_F32) || EPI == EPI_PARTIAL) {
+    epilogue_f32_direct<BM, BN, NW, EPI == EPI_PARTIAL>(d, acc, lane, wm, wn, m0, n0, nlen, KSEG ? 0 : sn, split);
+    return;
+  }
   epilogue<BM, BN, EPI, OUT_F32, true, DUAL, NW>(d, acc, ep, lane, wm, wn, m0, n0, nlen, KSEG ? 0 : sn, split);
 }
 
