@@ -220,6 +220,78 @@ __global__ void __launch_bounds__(SP_THREADS) sp_ln_fwd_kernel(SpArgs a) {
   }
 }
 
+// Rows of at most 8192 columns (h % 8 == 0), several rows per workgroup: the
+// next row's y, x and mask are loaded before this row's stores are issued, so
+// they arrive while the stores drain (a wave's memory operations retire in
+// issue order, so loads issued after the stores would wait for them).  gamma
+// and beta stay in registers for all the rows.
+__global__ void __launch_bounds__(SP_THREADS) sp_ln_fwd_pipe_kernel(SpArgs a) {
+  __shared__ float red[4];
+  const int h = (int)a.h;
+  int64_t r = blockIdx.x;
+  if (r >= a.n) return;
+  u32x4 gw[SP_VPT], bw[SP_VPT], yw[SP_VPT], xw[SP_VPT];
+  uint2 mw[SP_VPT];
+  auto fetch = [&](int64_t row) {
+#pragma unroll
+    for (int i = 0; i < SP_VPT; ++i) {
+      yw[i] = raw8<true>(a.y + row * a.h, i, h);
+      xw[i] = raw8<true>(a.x + row * a.h, i, h);
+      mw[i] = rawmask8<true>(a.mask + row * a.h, i, h);
+    }
+  };
+#pragma unroll
+  for (int i = 0; i < SP_VPT; ++i) {
+    gw[i] = raw8<true>(a.gamma, i, h);
+    bw[i] = raw8<true>(a.beta, i, h);
+  }
+  fetch(r);
+  for (; r < a.n; r += gridDim.x) {
+    float u[SP_VPT][8];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < SP_VPT; ++i) {
+      float yv[8], xv[8];
+      unpack8(yw[i], yv);
+      unpack8(xw[i], xv);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        u[i][q] = fmaf(yv[q] * mask_at(mw[i], q), a.keep, xv[q]);
+        s += u[i][q];
+      }
+    }
+    const int64_t nr = r + gridDim.x;
+    if (nr < a.n) fetch(nr);  // in flight during the reductions and this row's stores
+    const float mean = block_sum(s, red) / (float)h;
+    float v2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < SP_VPT; ++i)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const bool in = col_of<true>(i, q) < h;
+        const float d = u[i][q] - mean;
+        v2 += in ? d * d : 0.f;
+      }
+    const float var = block_sum(v2, red) / (float)h;
+    const float rstd = 1.f / sqrtf(var + a.eps);
+    uint16_t *ur = a.uo + r * a.h, *zr = a.z + r * a.h;
+#pragma unroll
+    for (int i = 0; i < SP_VPT; ++i) {
+      float zv[8], gv[8], bv[8];
+      unpack8(gw[i], gv);
+      unpack8(bw[i], bv);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) zv[q] = fmaf((u[i][q] - mean) * rstd, gv[q], bv[q]);
+      store8<true>(ur, i, h, u[i]);
+      store8<true>(zr, i, h, zv);
+    }
+    if (threadIdx.x == 0) {
+      a.mean[r] = mean;
+      a.rstd[r] = rstd;
+    }
+  }
+}
+
 template <bool VEC, int NP>
 __global__ void __launch_bounds__(SP_THREADS) sp_ln_bwd_kernel(SpArgs a) {
   __shared__ float red[4];
@@ -268,6 +340,7 @@ __global__ void __launch_bounds__(SP_THREADS) sp_ln_bwd_kernel(SpArgs a) {
 // dgamma / dbeta partial column sums over one chunk of SP_RCHUNK rows (rows in
 // increasing order): thread i of the grid's x dimension owns columns 8i .. 8i+7.
 constexpr int SP_RCHUNK = 16;
+constexpr int SP_PIPE_WGS = 512;  // workgroups of the pipelined row kernel (two per CU)
 __global__ void __launch_bounds__(256) sp_ln_param_partial_kernel(SpArgs a) {
   const int64_t c0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
   if (c0 >= a.h) return;
@@ -346,6 +419,11 @@ __global__ void __launch_bounds__(256) sp_ln_param_reduce_kernel(const float *__
 
 template <int NP>
 hipError_t launch_fwd(const SpArgs &a, bool vec, hipStream_t st) {
+  if (NP == 1 && vec) {  // several rows per workgroup, pipelined
+    const unsigned grid = (unsigned)(a.n < SP_PIPE_WGS ? a.n : SP_PIPE_WGS);
+    hipLaunchKernelGGL(sp_ln_fwd_pipe_kernel, dim3(grid), dim3(SP_THREADS), 0, st, a);
+    return hipGetLastError();
+  }
   const unsigned grid = (unsigned)(a.n < 1048576 ? a.n : 1048576);
   if (vec) hipLaunchKernelGGL((sp_ln_fwd_kernel<true, NP>), dim3(grid), dim3(SP_THREADS), 0, st, a);
   else hipLaunchKernelGGL((sp_ln_fwd_kernel<false, NP>), dim3(grid), dim3(SP_THREADS), 0, st, a);
