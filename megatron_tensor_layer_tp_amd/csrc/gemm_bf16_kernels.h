@@ -199,6 +199,12 @@ __device__ __forceinline__ u32x4 pack8(const float *v) {
   return o;
 }
 
+// a run of 8 bf16 outputs; `nt` streams it past the caches (a non-temporal store)
+__device__ __forceinline__ void st8(uint16_t *p, u32x4 v, bool nt) {
+  if (nt) __builtin_nontemporal_store(v, (u32x4 *)p);
+  else *(u32x4 *)p = v;
+}
+
 __device__ __forceinline__ void unpack8(const u32x4 &w, float *v) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -292,12 +298,12 @@ __device__ __forceinline__ void epi8(const GemmDesc &d, int gm, int gn, int nlen
     uint16_t *O1 = (uint16_t *)d.ao1 + (int64_t)gm * d.ldao + gn;
     const bool w_o0 = (EPI == EPI_ACT_FWD && d.ao0) || EPI == EPI_SWIGLU_FWD || EPI == EPI_SWIGLU_BWD;
     if (full) {
-      *(u32x4 *)C = pack8(y);
+      st8(C, pack8(y), d.stream_out & 1);
       if constexpr (EPI == EPI_ACT_FWD || EPI == EPI_SWIGLU_FWD) {
-        if (w_o0) *(u32x4 *)O0 = pack8(x);
+        if (w_o0) st8(O0, pack8(x), d.stream_out & 2);
       }
-      if constexpr (EPI == EPI_SWIGLU_FWD) *(u32x4 *)O1 = pack8(u);
-      if constexpr (EPI == EPI_SWIGLU_BWD) *(u32x4 *)O0 = pack8(y2);
+      if constexpr (EPI == EPI_SWIGLU_FWD) st8(O1, pack8(u), d.stream_out & 4);
+      if constexpr (EPI == EPI_SWIGLU_BWD) st8(O0, pack8(y2), d.stream_out & 2);
     } else {
       for (int q = 0; q < cnt; ++q) {
         C[q] = tp_f2bf(y[q]);

@@ -353,6 +353,7 @@ struct Ptrs {
   void *ao0 = nullptr, *ao1 = nullptr;
   int64_t ldao = 0;
   int act = ACT_RELU;
+  int stream_out = 0;  // GemmDesc::stream_out
 };
 
 GemmDesc make_desc(const Spec &s, const Ptrs &q, const Plan &p, int dt, void *ws) {
@@ -395,6 +396,7 @@ GemmDesc make_desc(const Spec &s, const Ptrs &q, const Plan &p, int dt, void *ws
   d.tiles_n = p.tiles_n;
   d.group_m = 8;
   d.ws = (float *)ws;
+  d.stream_out = q.stream_out;
   return d;
 }
 
@@ -745,12 +747,14 @@ int tp_mlp_fwd(int act, int dt, int64_t s, int64_t h, int64_t ft, const void *X,
   p1.C[0] = H; p1.ldc[0] = ft;
   p1.ao0 = Z; p1.ldao = ft;
   p1.act = act == TP_ACT_GELU ? ACT_GELU : ACT_RELU;
+  p1.stream_out = 1 | 2;
   if (int e = run(g1, p1, dt, nullptr, st, "tp_mlp_fwd column GEMM")) return e;
   Spec g2 = spec_nn(s, h, ft, EPI_STORE);
   Ptrs p2;
   p2.A[0] = H; p2.lda[0] = ft;
   p2.B[0] = W2; p2.ldb[0] = h;
   p2.C[0] = Y; p2.ldc[0] = h;
+  p2.stream_out = 1;
   if (int e = run(g2, p2, dt, nullptr, st, "tp_mlp_fwd row GEMM")) return e;
   return ok();
 }
@@ -845,6 +849,7 @@ int tp_swiglu_fwd(int dt, int64_t s, int64_t h, int64_t ft, const void *X, const
     p.A[0] = A; p.lda[0] = ft;
     p.B[0] = Wd; p.ldb[0] = h;
     p.C[0] = Y; p.ldc[0] = h;
+    p.stream_out = 1;
     if (int e = run(g, p, dt, nullptr, st, "tp_swiglu_fwd down GEMM")) return e;
   }
   return ok();
@@ -889,6 +894,8 @@ int tp_swiglu_bwd(int dt, int64_t s, int64_t h, int64_t ft, const void *X, const
     pa.C[0] = dG; pa.ldc[0] = ft;
     pa.ai0 = G; pa.ai1 = U; pa.ldai = ft;
     pa.ao0 = dU; pa.ldao = ft;
+    pw.stream_out = 1;
+    pa.stream_out = 1 | 2;
     if (int e = run_pair(L.g_dwd, pw, L.g_da, pa, dt, part1, st, "tp_swiglu_bwd dWd GEMM", "tp_swiglu_bwd dA GEMM",
                          nullptr, &pend))
       return e;
@@ -902,6 +909,7 @@ int tp_swiglu_bwd(int dt, int64_t s, int64_t h, int64_t ft, const void *X, const
     px.A[0] = dG; px.A[1] = dU; px.lda[0] = px.lda[1] = ft;
     px.B[0] = Wg; px.B[1] = Wu; px.ldb[0] = px.ldb[1] = ft;
     px.C[0] = dX; px.ldc[0] = h;
+    pw.stream_out = px.stream_out = 1;
     if (int e = run_pair(L.g_dwgu, pw, L.g_dx, px, dt, part2, st, "tp_swiglu_bwd dWg/dWu GEMM",
                          "tp_swiglu_bwd dX GEMM", &pend))
       return e;
@@ -948,6 +956,7 @@ int tp_attn_proj_fwd(int dt, int64_t s, int64_t h, int64_t dq, int64_t dkv, cons
   po.A[0] = O; po.lda[0] = dq;
   po.B[0] = Wo; po.ldb[0] = h;
   po.C[0] = Y; po.ldc[0] = h;
+  pq.stream_out = po.stream_out = 1;
   if (int e = run_pair(gq, pq, go, po, dt, nullptr, st, "tp_attn_proj_fwd QKV GEMM", "tp_attn_proj_fwd output GEMM"))
     return e;
   return ok();
@@ -995,6 +1004,7 @@ int tp_attn_proj_bwd(int dt, int64_t s, int64_t h, int64_t dq, int64_t dkv, cons
     px.B[0] = Wq; px.B[1] = Wk; px.B[2] = Wv;
     px.ldb[0] = dq; px.ldb[1] = px.ldb[2] = dkv;
     px.C[0] = dX; px.ldc[0] = h;
+    pw.stream_out = px.stream_out = 1;
     if (int e = run_pair(L.g_dwqkv, pw, L.g_dx, px, dt, part1, st, "tp_attn_proj_bwd dWqkv GEMM",
                          "tp_attn_proj_bwd dX GEMM", nullptr, &pend))
       return e;
@@ -1008,6 +1018,7 @@ int tp_attn_proj_bwd(int dt, int64_t s, int64_t h, int64_t dq, int64_t dkv, cons
     po.A[0] = dY; po.lda[0] = h;
     po.B[0] = Wo; po.ldb[0] = h;
     po.C[0] = dO; po.ldc[0] = dq;
+    pw.stream_out = po.stream_out = 1;
     if (int e = run_pair(L.g_dwo, pw, L.g_do, po, dt, part2, st, "tp_attn_proj_bwd dWo GEMM",
                          "tp_attn_proj_bwd dO GEMM", &pend))
       return e;
