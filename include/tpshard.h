@@ -204,7 +204,9 @@ int tp_sp_ln_fwd(int dt, int64_t n, int64_t h, float p, float eps,
  *     dgamma = sum_r dz * xh,  dbeta = sum_r dz    (this slice's share; the
  *     shards' shares are summed across cards)
  * ws: scratch of tp_sp_ln_bwd_workspace(dt, n, h) bytes, 256-byte aligned
- * (partial column sums of each 16-row chunk, reduced in a fixed order). */
+ * (partial column sums of dgamma and dbeta, each over a fixed set of rows in
+ * increasing order, reduced in a fixed order: rows h <= 8192 with h % 8 == 0
+ * give min(n, 256) partials, others one per 16-row chunk). */
 size_t tp_sp_ln_bwd_workspace(int dt, int64_t n, int64_t h);
 int tp_sp_ln_bwd(int dt, int64_t n, int64_t h, float p,
                  const void *dz, const void *dun, const void *u,

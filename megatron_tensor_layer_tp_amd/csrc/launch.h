@@ -81,7 +81,7 @@ hipError_t tp_launch_attn_fwd(int64_t s, int64_t nq, int64_t nkv, const void *Q,
 
 // sequence-parallel region (residual + dropout + LayerNorm) on [n, h] bf16 rows
 int tp_sp_ln_passes(int64_t h);        // register passes per row (h <= 8192: 1)
-int tp_sp_ln_bwd_grid(int64_t n);      // row chunks of the backward = partial sums of dgamma/dbeta
+int tp_sp_ln_bwd_grid(int64_t n, int64_t h);  // partial sums of dgamma/dbeta the backward writes
 hipError_t tp_launch_sp_ln_fwd(int64_t n, int64_t h, float keep, float eps, const void *y, const void *x,
                                const uint8_t *mask, const void *gamma, const void *beta, void *u, void *z,
                                float *mean, float *rstd, hipStream_t st);

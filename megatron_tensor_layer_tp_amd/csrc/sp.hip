@@ -13,9 +13,12 @@
 // the row is loaded once into registers (16-byte loads of 8 bf16 when h is a
 // multiple of 8), the row statistics are exact two-pass sums over those
 // registers (wave shuffles, then LDS across the 4 waves), and every output is
-// written once.  The backward's dgamma / dbeta are column sums over the rows:
-// a second kernel sums chunks of 16 rows per column (16-byte loads across the
-// row) into partials that a third reduces in chunk order (deterministic).
+// written once.  The backward's dgamma / dbeta are column sums over the rows.
+// For rows of up to 8192 columns in 16-byte vectors the row kernel keeps them:
+// each of its 256 workgroups sums its own rows (in increasing order) in
+// registers and writes one partial; otherwise a second kernel sums chunks of 16
+// rows per column into partials.  Either way a last kernel reduces the partials
+// in a fixed order (deterministic).
 #include "launch.h"
 
 namespace {
@@ -337,6 +340,117 @@ __global__ void __launch_bounds__(SP_THREADS) sp_ln_bwd_kernel(SpArgs a) {
   }
 }
 
+// The backward for rows of up to 8192 columns (16-byte vectors): every workgroup
+// (512 threads, two 8-element vectors of the row each) takes rows blockIdx.x,
+// blockIdx.x + G, ... (G = gridDim.x), issues the next row's loads before this
+// row's reductions and stores, and keeps its running dgamma / dbeta column sums
+// (its rows in increasing order) in registers; it writes them once, as partial
+// sums part[blockIdx.x][2][h], at the end.
+constexpr int SP_BWD_WGS = 256;    // workgroups of the pipelined backward (one per CU)
+constexpr int SP_BWD_THREADS = 512;
+constexpr int SP_BWD_VPT = 2;      // 2 x 8 x 512 = 8192 columns
+__global__ void __launch_bounds__(SP_BWD_THREADS) sp_ln_bwd_pipe_kernel(SpArgs a) {
+  __shared__ float red[8];
+  const int h = (int)a.h;
+  const int tid = threadIdx.x;
+  auto col = [&](int i) { return 8 * (tid + SP_BWD_THREADS * i); };
+  auto sum = [&](float v) {  // over the workgroup, every thread gets the total
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    __syncthreads();
+    if ((tid & 63) == 0) red[tid >> 6] = v;
+    __syncthreads();
+    return ((red[0] + red[1]) + (red[2] + red[3])) + ((red[4] + red[5]) + (red[6] + red[7]));
+  };
+  auto raw = [&](const uint16_t *row, int i) {
+    const int c = col(i);
+    return c < h ? *(const u32x4 *)(row + c) : u32x4{0u, 0u, 0u, 0u};
+  };
+  float pg[SP_BWD_VPT][8], pb[SP_BWD_VPT][8];
+#pragma unroll
+  for (int i = 0; i < SP_BWD_VPT; ++i)
+#pragma unroll
+    for (int q = 0; q < 8; ++q) pg[i][q] = pb[i][q] = 0.f;
+  u32x4 gw[SP_BWD_VPT], uw[SP_BWD_VPT], zw[SP_BWD_VPT], nw[SP_BWD_VPT];
+  uint2 mw[SP_BWD_VPT];
+  float mean = 0.f, rstd = 0.f;
+  auto fetch = [&](int64_t row) {
+#pragma unroll
+    for (int i = 0; i < SP_BWD_VPT; ++i) {
+      uw[i] = raw(a.u + row * a.h, i);
+      zw[i] = raw(a.dz + row * a.h, i);
+      nw[i] = raw(a.dun + row * a.h, i);
+      const int c = col(i);
+      mw[i] = c < h ? *(const uint2 *)(a.mask + row * a.h + c) : make_uint2(0u, 0u);
+    }
+    mean = a.mean[row];
+    rstd = a.rstd[row];
+  };
+#pragma unroll
+  for (int i = 0; i < SP_BWD_VPT; ++i) gw[i] = raw(a.gamma, i);
+  int64_t r = blockIdx.x;
+  if (r < a.n) fetch(r);
+  for (; r < a.n; r += gridDim.x) {
+    float xh[SP_BWD_VPT][8], g[SP_BWD_VPT][8];
+    float sg = 0.f, sgx = 0.f;
+    const float rm = mean, rr = rstd;
+#pragma unroll
+    for (int i = 0; i < SP_BWD_VPT; ++i) {
+      float uv[8], dzv[8], gv[8];
+      unpack8(uw[i], uv);
+      unpack8(zw[i], dzv);
+      unpack8(gw[i], gv);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const bool in = col(i) + q < h;
+        xh[i][q] = in ? (uv[q] - rm) * rr : 0.f;
+        g[i][q] = dzv[q] * gv[q];
+        sg += g[i][q];
+        sgx += g[i][q] * xh[i][q];
+        pg[i][q] = fmaf(dzv[q], xh[i][q], pg[i][q]);
+        pb[i][q] += dzv[q];
+      }
+    }
+    u32x4 dn[SP_BWD_VPT];
+    uint2 mk[SP_BWD_VPT];
+#pragma unroll
+    for (int i = 0; i < SP_BWD_VPT; ++i) {
+      dn[i] = nw[i];
+      mk[i] = mw[i];
+    }
+    const int64_t nr = r + gridDim.x;
+    if (nr < a.n) fetch(nr);  // in flight during the reductions and this row's stores
+    const float mg = sum(sg) / (float)h;
+    const float mgx = sum(sgx) / (float)h;
+#pragma unroll
+    for (int i = 0; i < SP_BWD_VPT; ++i) {
+      float dxv[8], dyv[8], dnv[8];
+      unpack8(dn[i], dnv);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        dxv[q] = fmaf(rr, g[i][q] - mg - xh[i][q] * mgx, dnv[q]);
+        dyv[q] = dxv[q] * mask_at(mk[i], q) * a.keep;
+      }
+      const int c = col(i);
+      if (c < h) {
+        *(u32x4 *)(a.dx + r * a.h + c) = pack8(dxv);
+        *(u32x4 *)(a.dy + r * a.h + c) = pack8(dyv);
+      }
+    }
+  }
+  float *pr = a.part + (int64_t)blockIdx.x * 2 * a.h;
+#pragma unroll
+  for (int i = 0; i < SP_BWD_VPT; ++i) {
+    const int c = col(i);
+    if (c < h) {
+      *(float4 *)(pr + c) = make_float4(pg[i][0], pg[i][1], pg[i][2], pg[i][3]);
+      *(float4 *)(pr + c + 4) = make_float4(pg[i][4], pg[i][5], pg[i][6], pg[i][7]);
+      *(float4 *)(pr + a.h + c) = make_float4(pb[i][0], pb[i][1], pb[i][2], pb[i][3]);
+      *(float4 *)(pr + a.h + c + 4) = make_float4(pb[i][4], pb[i][5], pb[i][6], pb[i][7]);
+    }
+  }
+}
+
 // dgamma / dbeta partial column sums over one chunk of SP_RCHUNK rows (rows in
 // increasing order): thread i of the grid's x dimension owns columns 8i .. 8i+7.
 constexpr int SP_RCHUNK = 16;
@@ -441,7 +555,11 @@ hipError_t launch_bwd(const SpArgs &a, bool vec, hipStream_t st) {
 
 int tp_sp_ln_passes(int64_t h) { return (int)((h + SP_VPT * 8 * SP_THREADS - 1) / (SP_VPT * 8 * SP_THREADS)); }
 
-int tp_sp_ln_bwd_grid(int64_t n) {
+// the pipelined backward serves rows of up to 8192 columns in 16-byte vectors
+static bool sp_bwd_pipe(int64_t n, int64_t h) { return n > 0 && h % 8 == 0 && tp_sp_ln_passes(h) == 1; }
+
+int tp_sp_ln_bwd_grid(int64_t n, int64_t h) {
+  if (sp_bwd_pipe(n, h)) return (int)(n < SP_BWD_WGS ? n : SP_BWD_WGS);
   const int64_t chunks = (n + SP_RCHUNK - 1) / SP_RCHUNK;
   return (int)(chunks > 0 ? chunks : 1);
 }
@@ -491,8 +609,17 @@ hipError_t tp_launch_sp_ln_bwd(int64_t n, int64_t h, float keep, const void *dz,
   a.dy = (uint16_t *)dy;
   a.part = part;
   const bool vec = h % 8 == 0;
-  const int chunks = tp_sp_ln_bwd_grid(n);
+  const int chunks = tp_sp_ln_bwd_grid(n, h);
   hipError_t e = hipSuccess;
+  if (sp_bwd_pipe(n, h)) {
+    // rows, and their partial column sums, in one kernel; then the fixed-order reduction
+    hipLaunchKernelGGL(sp_ln_bwd_pipe_kernel, dim3((unsigned)chunks), dim3(SP_BWD_THREADS), 0, st, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t rb = (h + 255) / 256;
+    hipLaunchKernelGGL(sp_ln_param_reduce_kernel, dim3((unsigned)(rb < 65536 ? rb : 65536)), dim3(256), 0, st,
+                       part, chunks, h, (uint16_t *)dgamma, (uint16_t *)dbeta);
+    return hipGetLastError();
+  }
   if (n > 0) {
     switch (tp_sp_ln_passes(h)) {
     case 1: e = launch_bwd<1>(a, vec, st); break;

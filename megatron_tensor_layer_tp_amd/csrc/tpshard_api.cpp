@@ -1124,7 +1124,7 @@ size_t tp_sp_ln_bwd_workspace(int dt, int64_t n, int64_t h) {
   c.dtype(dt, false, "tp_sp_ln_bwd_workspace");
   c.dim(n, "n") && c.dim(h, "h");
   if (c.status) return 0;
-  return align256((size_t)tp_sp_ln_bwd_grid(n) * 2 * h * sizeof(float));
+  return align256((size_t)tp_sp_ln_bwd_grid(n, h) * 2 * h * sizeof(float));
 }
 
 int tp_sp_ln_bwd(int dt, int64_t n, int64_t h, float p, const void *dz, const void *dun, const void *u,
@@ -1141,7 +1141,7 @@ int tp_sp_ln_bwd(int dt, int64_t n, int64_t h, float p, const void *dz, const vo
       c.ptr(rstd, n, "rstd") && c.ptr(gamma, h, "gamma") && c.ptr(mask, ne, "mask") && c.ptr(dx, ne, "dx") &&
       c.ptr(dy, ne, "dy") && c.ptr(dgamma, h, "dgamma") && c.ptr(dbeta, h, "dbeta");
   if (c.status) return c.status;
-  ws_ok(c, ws, ws_bytes, h ? align256((size_t)tp_sp_ln_bwd_grid(n) * 2 * h * sizeof(float)) : 0, "tp_sp_ln_bwd");
+  ws_ok(c, ws, ws_bytes, h ? align256((size_t)tp_sp_ln_bwd_grid(n, h) * 2 * h * sizeof(float)) : 0, "tp_sp_ln_bwd");
   if (c.status) return c.status;
   hipError_t e = tp_launch_sp_ln_bwd(n, h, 1.f / (1.f - p), dz, dun, u, mean, rstd, gamma, mask, dx, dy, dgamma,
                                      dbeta, (float *)ws, (hipStream_t)stream);

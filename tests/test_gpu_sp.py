@@ -76,7 +76,7 @@ def check(got, want, d, rows=None):
 
 
 @pytest.mark.parametrize("n,h,p", [(33, 768, 0.1), (17, 1000, 0.0), (5, 130, 0.1), (9, 8, 0.5), (3, 12000, 0.1),
-                                   (1, 8192, 0.1)])
+                                   (1, 8192, 0.1), (300, 1016, 0.1), (600, 64, 0.2)])
 def test_sp_small(oracle_mod, n, h, p):
     d = I.sp_inputs(4, n=n, h=h, p=p)
     check(run_sp(d), oracle_sp(oracle_mod, d), d)
