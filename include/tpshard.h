@@ -62,7 +62,7 @@ typedef enum {
     TP_EALIGN = 4,        /* a pointer is not 16-byte aligned */
     TP_EWORKSPACE = 5,    /* workspace missing or smaller than the size query */
     TP_EHIP = 6,          /* the HIP runtime reported an error at launch */
-    TP_EUNSUPPORTED = 7   /* valid request this build does not implement */
+    TP_EUNSUPPORTED = 7   /* valid request the library does not implement */
 } tp_status;
 
 typedef enum { TP_DT_F32 = 0, TP_DT_BF16 = 1 } tp_dtype;
