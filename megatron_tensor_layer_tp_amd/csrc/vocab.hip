@@ -13,6 +13,9 @@
 // 256-thread workgroup which issues all of its 16-byte loads for the row up
 // front (16 per thread covers a 16384-float row), takes the exact row max,
 // then sums exp(z - max) from registers: the logits are read from HBM once.
+// The logits are read, and the CE gradient written, with non-temporal
+// accesses: each byte is touched once, and keeping it out of the caches keeps
+// their dirty lines from being written back under the next kernel.
 #include "launch.h"
 
 namespace {
@@ -52,7 +55,7 @@ __global__ void __launch_bounds__(CE_THREADS) vocab_ce_kernel(const float *__res
 #pragma unroll
       for (int i = 0; i < CE_PER; ++i) {
         const int64_t idx = base + tid + (int64_t)CE_THREADS * i;
-        if (idx < nvec) v[i] = p[idx];
+        if (idx < nvec) v[i] = __builtin_nontemporal_load(p + idx);
         else
 #pragma unroll
           for (int e = 0; e < VW; ++e) v[i][e] = -INFINITY;
@@ -118,7 +121,7 @@ __global__ void __launch_bounds__(CE_THREADS) vocab_ce_bwd_kernel(const float *_
     const vec_t *p = (const vec_t *)(z + row * Vs);
 #pragma unroll 4
     for (int64_t i = threadIdx.x; i < nvec; i += CE_THREADS) {
-      const vec_t v = p[i];
+      const vec_t v = __builtin_nontemporal_load(p + i);
       float o[VW];
 #pragma unroll
       for (int e = 0; e < VW; ++e) {
@@ -131,10 +134,10 @@ __global__ void __launch_bounds__(CE_THREADS) vocab_ce_bwd_kernel(const float *_
           typedef float f2 __attribute__((ext_vector_type(2)));
           typedef __bf16 b2 __attribute__((ext_vector_type(2)));
           const f2 lo = {o[0], o[1]}, hi = {o[2], o[3]};
-          uint2 w;
-          w.x = __builtin_bit_cast(uint32_t, __builtin_convertvector(lo, b2));
-          w.y = __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, b2));
-          *(uint2 *)dst = w;
+          typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+          const u2 w = {__builtin_bit_cast(uint32_t, __builtin_convertvector(lo, b2)),
+                        __builtin_bit_cast(uint32_t, __builtin_convertvector(hi, b2))};
+          __builtin_nontemporal_store(w, (u2 *)dst);
         } else {
           dst[0] = __builtin_bit_cast(uint16_t, (__bf16)o[0]);
         }
@@ -142,7 +145,7 @@ __global__ void __launch_bounds__(CE_THREADS) vocab_ce_bwd_kernel(const float *_
         vec_t w;
 #pragma unroll
         for (int e = 0; e < VW; ++e) w[e] = o[e];
-        *((vec_t *)((float *)out + row * Vs) + i) = w;
+        __builtin_nontemporal_store(w, (vec_t *)((float *)out + row * Vs) + i);
       }
     }
   }
