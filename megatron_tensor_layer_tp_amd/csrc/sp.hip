@@ -161,6 +161,19 @@ __device__ __forceinline__ float mask_at(const uint2 &m, int q) {
   return (float)(((q < 4 ? m.x : m.y) >> (8 * (q & 3))) & 0xffu);
 }
 
+// the same 16-byte row loads, non-temporal: the forward reads each row once
+// (22 -> 18.4 us on the c4 slice in the step; the backward measured 3% slower
+// with them and keeps plain loads)
+__device__ __forceinline__ u32x4 raw8_nt(const uint16_t *row, int c, int h) {
+  return c < h ? __builtin_nontemporal_load((const u32x4 *)(row + c)) : u32x4{0u, 0u, 0u, 0u};
+}
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 rawmask8_nt(const uint8_t *row, int c, int h) {
+  if (c >= h) return make_uint2(0u, 0u);
+  const u32x2 m = __builtin_nontemporal_load((const u32x2 *)(row + c));
+  return make_uint2(m[0], m[1]);
+}
+
 struct SpArgs {
   int64_t n, h;
   float keep, eps;  // 1 / (1 - p), LayerNorm epsilon
@@ -238,9 +251,9 @@ __global__ void __launch_bounds__(SP_THREADS) sp_ln_fwd_pipe_kernel(SpArgs a) {
   auto fetch = [&](int64_t row) {
 #pragma unroll
     for (int i = 0; i < SP_VPT; ++i) {
-      yw[i] = raw8<true>(a.y + row * a.h, i, h);
-      xw[i] = raw8<true>(a.x + row * a.h, i, h);
-      mw[i] = rawmask8<true>(a.mask + row * a.h, i, h);
+      yw[i] = raw8_nt(a.y + row * a.h, col_of<true>(i, 0), h);
+      xw[i] = raw8_nt(a.x + row * a.h, col_of<true>(i, 0), h);
+      mw[i] = rawmask8_nt(a.mask + row * a.h, col_of<true>(i, 0), h);
     }
   };
 #pragma unroll
