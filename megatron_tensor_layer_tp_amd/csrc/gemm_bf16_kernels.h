@@ -809,12 +809,14 @@ __device__ __forceinline__ bf16x8 read_tr(const char *p0, const char *p1) {
 // The whole tile computation of the DMA kernel for logical tile id `lid`;
 // smem0 / smem1 are the two LDS stages (each at least 128 * (BM + BN) bytes)
 // declared by the calling kernel.
-template <int BM, int BN, bool A_KC, bool B_KC, int EPI, bool OUT_F32, bool KSEG, int NW = 4, int NS = 2>
+template <int BM, int BN, bool A_KC, bool B_KC, int EPI, bool OUT_F32, bool KSEG, int NW = 4, int NS = 2,
+          bool A3 = false>
 __device__ __forceinline__ void dma_body(const GemmDesc &d, int lid, char *smem0, char *smem1,
                                          char *smem2 = nullptr) {
   static_assert(NS == 2 || NS == 3, "two or three LDS stages");
   constexpr bool DUAL = EPI == EPI_SWIGLU_FWD;
   static_assert(!(DUAL && (B_KC || KSEG)), "the dual gate/up operand is an n-contiguous weight");
+  static_assert(!A3 || (NS == 2 && !KSEG && !DUAL), "three A stages: two-stage single-B products");
   // NW waves in a 2 x NW/2 grid, each a (BM/2) x (BN/(NW/2)) sub-tile
   constexpr int WGN = NW / 2;
   constexpr int WTM = BM / 2, WTN = BN / WGN, FM = WTM / 32, FN = WTN / 32;
@@ -969,7 +971,93 @@ __device__ __forceinline__ void dma_body(const GemmDesc &d, int lid, char *smem0
   const uint32_t L0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(smem0));
   const uint32_t L1 = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(smem1));
   const int nk = kt_end - kt_begin;
-  if constexpr (NS == 2) {
+  if constexpr (A3) {
+    // Three A stages and two B stages in [A0 | A1 | A2 | B0 | B1]: step t stages B of
+    // tile t+1 and then A of tile t+2 (each into the buffer step t-1 used), so an A
+    // tile has two steps to land.  The waves' DMAs retire in issue order, so waiting
+    // until at most A(t+1)'s are outstanding means A(t) and B(t) have landed.
+    char *const abase = smem0, *const bbase = smem0 + 3 * 128 * BM;
+    const uint32_t LA = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(abase));
+    const uint32_t LB = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_addr(bbase));
+    int kA = k0, kB = k0;
+    auto prepA = [&]() {
+      rsa = rsrc_words(A_KC ? Ab + (int64_t)m0 * lda + kA : Ab + (int64_t)kA * lda + m0);
+      da.offsets(oa, klen - kA, wid, lane);
+      kA += BK;
+    };
+    auto prepB = [&]() {
+      rsb = rsrc_words(B_KC ? Bb + (int64_t)n0 * ldb + kB : Bb + (int64_t)kB * ldb + n0);
+      db.offsets(ob, klen - kB, wid, lane);
+      kB += BK;
+    };
+    // A's fragments from SA, B's from SB (B offsets carry the 128 * BM of a whole stage)
+    auto load_frags2 = [&](const char *SA, const char *SB, int kk, bf16x8 *af, bf16x8 *bfr) {
+      const char *SBv = SB - 128 * BM;
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        if constexpr (A_KC) af[fm] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(SA + aoff[kk] + fm * 32 * 128));
+        else af[fm] = read_tr(SA + arc[fm][0] + kk * 16 * 2 * BM, SA + arc[fm][1] + kk * 16 * 2 * BM);
+      }
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        if constexpr (B_KC) bfr[fn] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(SBv + boff[kk] + fn * 32 * 128));
+        else bfr[fn] = read_tr(SBv + brc[fn][0] + kk * 16 * 2 * BN, SBv + brc[fn][1] + kk * 16 * 2 * BN);
+      }
+    };
+    if (nk > 0) {
+      prepA();
+#pragma unroll
+      for (int i = 0; i < DA::NI; ++i) da.issue(rsa, oa, i, LA, wid);
+      prepB();
+#pragma unroll
+      for (int i = 0; i < DB::NI; ++i) db.issue(rsb, ob, i, LB, wid);
+    }
+    if (nk > 1) {
+      prepA();
+#pragma unroll
+      for (int i = 0; i < DA::NI; ++i) da.issue(rsa, oa, i, LA + 128 * BM, wid);
+    }
+    int sa = 0;  // A stage of tile t
+    for (int t = 0; t < nk; ++t) {
+      if (t + 1 < nk) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(DA::NI) : "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      lds_barrier();
+      const char *SA = abase + sa * 128 * BM, *SB = bbase + (t & 1) * 128 * BN;
+      const bool moreB = t + 1 < nk, moreA = t + 2 < nk;
+      const uint32_t nB = LB + ((t + 1) & 1) * 128 * BN;
+      const uint32_t nA = LA + (sa == 0 ? 2 : sa - 1) * 128 * BM;  // stage (t + 2) % 3
+      bf16x8 fa[2][FM], fb[2][FN];
+      load_frags2(SA, SB, 0, fa[0], fb[0]);
+      if (moreB) prepB();
+      if (moreA) prepA();
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        if (kk < 3) load_frags2(SA, SB, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn)
+            acc[fm][fn] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][fm], fb[kk & 1][fn], acc[fm][fn], 0, 0, 0);
+          if (kk < 2) {
+            const int g = kk * FM + fm;
+#pragma unroll
+            for (int p = 0; p < PER; ++p) {
+              const int q = g * PER + p;  // B's DMAs first, then A's
+              if (q < DB::NI) {
+                if (moreB) db.issue(rsb, ob, q, nB, wid);
+              } else if (q < NLD) {
+                if (moreA) da.issue(rsa, oa, q - DB::NI, nA, wid);
+              }
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      sa = sa == 2 ? 0 : sa + 1;
+    }
+  } else if constexpr (NS == 2) {
     if (nk > 0) {
       prep();
 #pragma unroll
@@ -1090,8 +1178,11 @@ __global__ void __launch_bounds__(64 * res_waves(RES))
 __attribute__((amdgpu_waves_per_eu(res_wpe(RES), res_wpe(RES)))) gemm_dma_kernel(GemmDesc d) {
   static_assert(res_fits(BM, BN, RES), "LDS stages exceed the CU's 160 KB");
   constexpr int S = 128 * (BM + BN), NS = res_stages(RES);
-  __shared__ __attribute__((aligned(1024))) char smem[NS * S];
-  dma_body<BM, BN, A_KC, B_KC, EPI, OUT_F32, KSEG, res_waves(RES), NS>(
+  // one 8-wave workgroup per CU: the LDS left over by two stages takes a third A stage
+  constexpr bool A3 = RES == RES_WAVES8 && !KSEG && EPI != EPI_SWIGLU_FWD && 128 * (3 * BM + 2 * BN) <= 160 * 1024;
+  constexpr int LDS = A3 ? 128 * (3 * BM + 2 * BN) : NS * S;
+  __shared__ __attribute__((aligned(1024))) char smem[LDS];
+  dma_body<BM, BN, A_KC, B_KC, EPI, OUT_F32, KSEG, res_waves(RES), NS, A3>(
       d, xcd_lid(blockIdx.x, gridDim.x), smem, smem + S, NS == 3 ? smem + 2 * S : nullptr);
 }
 
