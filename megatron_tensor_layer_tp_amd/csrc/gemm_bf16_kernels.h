@@ -1164,9 +1164,12 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmDesc d) {
 template <int BM_, int BN_, bool A_KC_, bool B_KC_, int EPI_, bool OUT_F32_, bool KSEG_>
 struct Cfg {
   static constexpr int STAGE = 128 * (BM_ + BN_);
-  template <int NS, int NW>
+  // LDS of three A stages and two B stages (the A-deep pipeline of single-B products)
+  static constexpr int A3_LDS = 128 * (3 * BM_ + 2 * BN_);
+  static constexpr bool A3_OK = !KSEG_ && EPI_ != EPI_SWIGLU_FWD;
+  template <int NS, int NW, bool A3 = false>
   static __device__ __forceinline__ void run(const GemmDesc &d, int lid, char *s0, char *s1, char *s2) {
-    dma_body<BM_, BN_, A_KC_, B_KC_, EPI_, OUT_F32_, KSEG_, NW, NS>(d, lid, s0, s1, s2);
+    dma_body<BM_, BN_, A_KC_, B_KC_, EPI_, OUT_F32_, KSEG_, NW, NS, A3>(d, lid, s0, s1, s2);
   }
 };
 
@@ -1200,7 +1203,11 @@ __attribute__((amdgpu_waves_per_eu(res_wpe(RES), res_wpe(RES)))) gemm_dma_pair_k
                                                                                       GemmDesc d3, int n3) {
   constexpr int S = C1::STAGE > C2::STAGE ? C1::STAGE : C2::STAGE, NS = res_stages(RES);
   static_assert(NS * res_wgs(RES) * S <= 160 * 1024, "LDS stages exceed the CU's 160 KB");
-  __shared__ __attribute__((aligned(1024))) char smem[NS * S];
+  // with one 8-wave workgroup per CU, a product that can takes a third A stage
+  constexpr bool A3_1 = RES == RES_WAVES8 && C1::A3_OK && C1::A3_LDS <= 160 * 1024;
+  constexpr bool A3_2 = RES == RES_WAVES8 && C2::A3_OK && C2::A3_LDS <= 160 * 1024;
+  constexpr int L1 = A3_1 ? C1::A3_LDS : NS * S, L2 = A3_2 ? C2::A3_LDS : NS * S;
+  __shared__ __attribute__((aligned(1024))) char smem[L1 > L2 ? L1 : L2];
   char *s2 = NS == 3 ? smem + 2 * S : nullptr;
   const int b = blockIdx.x;
   if (b >= n1 + n2) {
@@ -1210,10 +1217,10 @@ __attribute__((amdgpu_waves_per_eu(res_wpe(RES), res_wpe(RES)))) gemm_dma_pair_k
   }
   const bool remap = (n1 & 7) == 0;
   if (b < n1) {
-    C1::template run<NS, res_waves(RES)>(d1, remap ? xcd_lid(b, n1) : b, smem, smem + S, s2);
+    C1::template run<NS, res_waves(RES), A3_1>(d1, remap ? xcd_lid(b, n1) : b, smem, smem + S, s2);
   } else {
     const int r = b - n1;
-    C2::template run<NS, res_waves(RES)>(d2, remap ? xcd_lid(r, n2) : r, smem, smem + S, s2);
+    C2::template run<NS, res_waves(RES), A3_2>(d2, remap ? xcd_lid(r, n2) : r, smem, smem + S, s2);
   }
 }
 
