@@ -18,7 +18,9 @@
 // each of its 256 workgroups sums its own rows (in increasing order) in
 // registers and writes one partial; otherwise a second kernel sums chunks of 16
 // rows per column into partials.  Either way a last kernel reduces the partials
-// in a fixed order (deterministic).
+// in a fixed order (deterministic); when h is a multiple of 64 the row kernel
+// lays its partials out by 64-column block, so that each workgroup of that
+// reduction reads one contiguous run.
 #include "launch.h"
 
 namespace {
@@ -358,10 +360,13 @@ __global__ void __launch_bounds__(SP_THREADS) sp_ln_bwd_kernel(SpArgs a) {
 // blockIdx.x + G, ... (G = gridDim.x), issues the next row's loads before this
 // row's reductions and stores, and keeps its running dgamma / dbeta column sums
 // (its rows in increasing order) in registers; it writes them once, as partial
-// sums part[blockIdx.x][2][h], at the end.
+// sums, at the end: part[blockIdx.x][2][h], or with BLOCKED (h a multiple of
+// 64) part[2][h/64][gridDim.x][64], so that the reduction of one 64-column
+// block reads one contiguous run.
 constexpr int SP_BWD_WGS = 256;    // workgroups of the pipelined backward (one per CU)
 constexpr int SP_BWD_THREADS = 512;
 constexpr int SP_BWD_VPT = 2;      // 2 x 8 x 512 = 8192 columns
+template <bool BLOCKED>
 __global__ void __launch_bounds__(SP_BWD_THREADS) sp_ln_bwd_pipe_kernel(SpArgs a) {
   __shared__ float red[8];
   const int h = (int)a.h;
@@ -451,15 +456,23 @@ __global__ void __launch_bounds__(SP_BWD_THREADS) sp_ln_bwd_pipe_kernel(SpArgs a
       }
     }
   }
-  float *pr = a.part + (int64_t)blockIdx.x * 2 * a.h;
 #pragma unroll
   for (int i = 0; i < SP_BWD_VPT; ++i) {
     const int c = col(i);
     if (c < h) {
-      *(float4 *)(pr + c) = make_float4(pg[i][0], pg[i][1], pg[i][2], pg[i][3]);
-      *(float4 *)(pr + c + 4) = make_float4(pg[i][4], pg[i][5], pg[i][6], pg[i][7]);
-      *(float4 *)(pr + a.h + c) = make_float4(pb[i][0], pb[i][1], pb[i][2], pb[i][3]);
-      *(float4 *)(pr + a.h + c + 4) = make_float4(pb[i][4], pb[i][5], pb[i][6], pb[i][7]);
+      float *qg, *qb;
+      if constexpr (BLOCKED) {
+        const int64_t nb = h / 64, blk = ((int64_t)(c >> 6) * gridDim.x + blockIdx.x) * 64 + (c & 63);
+        qg = a.part + blk;
+        qb = a.part + nb * gridDim.x * 64 + blk;
+      } else {
+        qg = a.part + (int64_t)blockIdx.x * 2 * a.h + c;
+        qb = qg + a.h;
+      }
+      *(float4 *)qg = make_float4(pg[i][0], pg[i][1], pg[i][2], pg[i][3]);
+      *(float4 *)(qg + 4) = make_float4(pg[i][4], pg[i][5], pg[i][6], pg[i][7]);
+      *(float4 *)qb = make_float4(pb[i][0], pb[i][1], pb[i][2], pb[i][3]);
+      *(float4 *)(qb + 4) = make_float4(pb[i][4], pb[i][5], pb[i][6], pb[i][7]);
     }
   }
 }
@@ -541,6 +554,30 @@ __global__ void __launch_bounds__(256) sp_ln_param_reduce_kernel(const float *__
     }
     dgamma[c] = f2bf(sg);
     dbeta[c] = f2bf(sb);
+  }
+}
+
+// The same sums over the BLOCKED layout: workgroup (b, y) reduces columns
+// 64b .. 64b+63 of dgamma (y = 0) or dbeta (y = 1); wave j adds partials
+// j*per .. (j+1)*per-1 in increasing order (each of its loads is 64
+// consecutive floats, the wave's run contiguous), then the 4 wave sums are
+// added in wave order.
+__global__ void __launch_bounds__(256) sp_ln_param_reduce_blocked_kernel(const float *__restrict__ part, int nparts,
+                                                                         int64_t h, uint16_t *__restrict__ dgamma,
+                                                                         uint16_t *__restrict__ dbeta) {
+  __shared__ float acc[4][64];
+  const int ci = threadIdx.x & 63, j = threadIdx.x >> 6;
+  const int per = (nparts + 3) / 4, k0 = min(nparts, j * per), k1 = min(nparts, k0 + per);
+  const int64_t nb = h / 64;
+  const float *p = part + ((int64_t)blockIdx.y * nb + blockIdx.x) * nparts * 64 + ci;
+  float v = 0.f;
+#pragma unroll 8
+  for (int k = k0; k < k1; ++k) v += p[(int64_t)k * 64];
+  acc[j][ci] = v;
+  __syncthreads();
+  if (j == 0) {
+    const float t = (acc[0][ci] + acc[1][ci]) + (acc[2][ci] + acc[3][ci]);
+    (blockIdx.y ? dbeta : dgamma)[(int64_t)blockIdx.x * 64 + ci] = f2bf(t);
   }
 }
 
@@ -626,7 +663,14 @@ hipError_t tp_launch_sp_ln_bwd(int64_t n, int64_t h, float keep, const void *dz,
   hipError_t e = hipSuccess;
   if (sp_bwd_pipe(n, h)) {
     // rows, and their partial column sums, in one kernel; then the fixed-order reduction
-    hipLaunchKernelGGL(sp_ln_bwd_pipe_kernel, dim3((unsigned)chunks), dim3(SP_BWD_THREADS), 0, st, a);
+    if (h % 64 == 0) {
+      hipLaunchKernelGGL(sp_ln_bwd_pipe_kernel<true>, dim3((unsigned)chunks), dim3(SP_BWD_THREADS), 0, st, a);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      hipLaunchKernelGGL(sp_ln_param_reduce_blocked_kernel, dim3((unsigned)(h / 64), 2), dim3(256), 0, st, part,
+                         chunks, h, (uint16_t *)dgamma, (uint16_t *)dbeta);
+      return hipGetLastError();
+    }
+    hipLaunchKernelGGL(sp_ln_bwd_pipe_kernel<false>, dim3((unsigned)chunks), dim3(SP_BWD_THREADS), 0, st, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t rb = (h + 255) / 256;
     hipLaunchKernelGGL(sp_ln_param_reduce_kernel, dim3((unsigned)(rb < 65536 ? rb : 65536)), dim3(256), 0, st,
