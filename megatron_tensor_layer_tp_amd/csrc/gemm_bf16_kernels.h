@@ -1122,15 +1122,30 @@ __device__ __forceinline__ void splitk_reduce_body(const GemmDesc &d, int64_t fi
     float s[W];
 #pragma unroll
     for (int q = 0; q < W; ++q) s[q] = 0.f;
-    for (int k = 0; k < d.splits; ++k) {
-      const float *p = d.ws + ((int64_t)k * d.M + gm) * d.N + gc;
-      if constexpr (VEC) {
-        const float4 a = *(const float4 *)p, b = *(const float4 *)(p + 4);
-        s[0] += a.x; s[1] += a.y; s[2] += a.z; s[3] += a.w;
-        s[4] += b.x; s[5] += b.y; s[6] += b.z; s[7] += b.w;
-      } else {
-        s[0] += p[0];
-      }
+    // up to 8 splits' loads in flight before their sums (in split order)
+    for (int k0 = 0; k0 < d.splits; k0 += 8) {
+      float4 a[8], b[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (k0 + j < d.splits) {
+          const float *p = d.ws + ((int64_t)(k0 + j) * d.M + gm) * d.N + gc;
+          if constexpr (VEC) {
+            a[j] = *(const float4 *)p;
+            b[j] = *(const float4 *)(p + 4);
+          } else {
+            a[j].x = p[0];
+          }
+        }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (k0 + j < d.splits) {
+          if constexpr (VEC) {
+            s[0] += a[j].x; s[1] += a[j].y; s[2] += a[j].z; s[3] += a[j].w;
+            s[4] += b[j].x; s[5] += b[j].y; s[6] += b[j].z; s[7] += b[j].w;
+          } else {
+            s[0] += a[j].x;
+          }
+        }
     }
     int sg = 0;
     if (!d.kseg)
