@@ -165,23 +165,45 @@ __global__ void __launch_bounds__(256) ce_merge_kernel(const float *__restrict__
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= s) return;
   const float *w = ws + row * 3 * (int64_t)P;
-  float mx = -INFINITY;
-  for (int p = lane; p < P; p += 64) mx = fmaxf(mx, w[p]);
-  mx = wave_max(mx);
-  float sum = 0.f;
-  if (mx != -INFINITY) {
-    const float mb = mx * LOG2E;
-    for (int p = lane; p < P; p += 64) {
-      const float mp = w[p];
-      if (mp != -INFINITY) sum += w[P + p] * exp2f(fmaf(mp, LOG2E, -mb));
+  const int64_t y = tgt[row];
+  const bool own = y >= start && y - start < Vs;
+  float tl = 0.f;
+  if (lane == 0 && own) tl = w[2 * P + (y - start) / W];  // in flight with the partials
+  float mx = -INFINITY, sum = 0.f;
+  constexpr int U = 4;
+  if (P <= 64 * U) {  // every partial of the row in registers, loaded in one batch
+    float mv[U], sv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p = u * 64 + lane;
+      mv[u] = p < P ? w[p] : -INFINITY;
+      sv[u] = p < P ? w[P + p] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) mx = fmaxf(mx, mv[u]);
+    mx = wave_max(mx);
+    if (mx != -INFINITY) {
+      const float mb = mx * LOG2E;
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (mv[u] != -INFINITY) sum += sv[u] * exp2f(fmaf(mv[u], LOG2E, -mb));
+    }
+  } else {
+    for (int p = lane; p < P; p += 64) mx = fmaxf(mx, w[p]);
+    mx = wave_max(mx);
+    if (mx != -INFINITY) {
+      const float mb = mx * LOG2E;
+      for (int p = lane; p < P; p += 64) {
+        const float mp = w[p];
+        if (mp != -INFINITY) sum += w[P + p] * exp2f(fmaf(mp, LOG2E, -mb));
+      }
     }
   }
   sum = wave_sum(sum);
   if (lane == 0) {
-    const int64_t y = tgt[row];
     m_out[row] = mx;
     se_out[row] = sum;
-    tl_out[row] = (y >= start && y - start < Vs) ? w[2 * P + (y - start) / W] : 0.f;
+    tl_out[row] = tl;
   }
 }
 
