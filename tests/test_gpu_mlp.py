@@ -111,6 +111,7 @@ EXACT_SHAPES = [
     (512, 384, 640),   # 16-byte loads, several tiles
     (264, 136, 264),   # 16-byte loads, tails of 8 past the tile edge
     (2048, 128, 256),  # long K for the weight gradients: split-K
+    (4104, 8, 8),      # one output tile, K long enough for more than 8 splits
     (520, 200, 1000),  # 128x192 tiles with ragged M, N (1000 = 5*192 + 40) and K edges
     (1032, 392, 776),  # 192-column tiles in the paired backward, ragged everywhere
     (1, 8, 8),
