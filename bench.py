@@ -6,18 +6,21 @@
 A step is one pass over every step of the shard path on seeded synthetic
 inputs already resident in HBM:
   * MLP shard forward + backward (column GEMM + GeLU, row GEMM, and the dZ /
-    dW2 / dX / dW1 GEMMs) at the GPT-2-small t=2 shard: s=8*1024, h=768,
-    f/t=1536 -- the workload the headline metric is quoted on;
+    dW2 / dX / dW1 GEMMs) at the GPT-3-175B t=8 shard: s=2048, h=12288,
+    f/t=6144 -- the workload the headline metric is quoted on -- and at the
+    GPT-2-small t=2 shard (s=8*1024, h=768, f/t=1536);
   * SwiGLU shard and attention projections, forward + backward, at the
     Llama-3-70B t=8 shard (s=8192, h=8192, f/t=3584, dq=1024, dkv=128);
   * vocab shard at V=128256, t=8: LM-head GEMM (fp32 logits [8192,16032]),
     cross-entropy statistics on those logits, and the embedding gather of
     8192 ids from a [16032,8192] table.
 Each library call is bracketed by HIP events on the stream it runs on.  One
-JSON line is printed: the headline is the MLP shard's forward+backward
-TFLOP/s; every row's time and throughput is listed under "rows"; "roofline"
-covers the longest single-kernel call (the LM-head GEMM) and "roofline_ce"
-the cross-entropy kernel; "cpu_baseline" times the fp64 oracle on a sample.
+JSON line is printed: the headline is the GPT-3-175B MLP shard's
+forward+backward TFLOP/s; every row's time and throughput is listed under
+"rows"; "roofline" covers the longest single-kernel call (the LM-head GEMM)
+and "roofline_ce" the cross-entropy kernel; "cpu_baseline" times the fp64
+oracle on a bounded sample of the headline workload, with "rows" beside it
+for the other rows.
 """
 from __future__ import annotations
 
@@ -178,36 +181,44 @@ def build_rows(torch, which, only=None):
     def want(*names):
         return only is None or only in names
 
-    # ---- MLP shard, GPT-2-small t=2 (the headline workload)
-    if want("mlp_fwd", "mlp_bwd"):
-        rows += mlp_rows(torch, up, bf, I, T)
+    # ---- MLP shard: GPT-3-175B t=8 (the headline workload) and GPT-2-small t=2
+    if want("mlp_fwd_gpt3", "mlp_bwd_gpt3"):
+        rows += mlp_rows(torch, up, bf, I, T, 3, "gpt3")
+        progress(f"inputs: {rows[-1].config} ready")
+    if want("mlp_fwd_gpt2", "mlp_bwd_gpt2"):
+        rows += mlp_rows(torch, up, bf, I, T, 2, "gpt2")
+        progress(f"inputs: {rows[-1].config} ready")
     if which == "mlp":
         return rows
     if want("swiglu_fwd", "swiglu_bwd", "attn_proj_fwd", "attn_proj_bwd", "attn_core_fwd", "sp_ln_fwd",
             "sp_ln_bwd"):
         rows += layer_rows(torch, up, bf, I, T, want)
+        progress(f"inputs: {rows[-1].config} ready")
     if want("lm_head_fwd", "vocab_ce", "vocab_embed", "vocab_ce_bwd", "lm_head_ce_fused"):
         rows += vocab_rows(torch, up, bf, I, T)
+        progress(f"inputs: {rows[-1].config} ready")
     return rows
 
 
-def mlp_rows(torch, up, bf, I, T):
+def mlp_rows(torch, up, bf, I, T, cfg, tag):
+    """MLP shard forward and backward (GeLU) of one workload, shard 0."""
     dev = "cuda:0"
     BF = T.TP_DT_BF16
     rows = []
-    d = I.mlp_inputs(2, shards=[0])
+    d = I.mlp_inputs(cfg, shards=[0])
     s, h, ft = d["s"], d["h"], d["ft"]
     X, W1, W2, dY = up(d["X"]), up(d["W1"][0]), up(d["W2"][0]), up(d["dY"])
     Z, H, Y = bf((s, ft)), bf((s, ft)), bf((s, h))
     dX, dW1, dW2 = bf((s, h)), bf((h, ft)), bf((ft, h))
     nb = T.tp_mlp_bwd_workspace(BF, s, h, ft)
     ws = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+    del d
     gf = 2.0 * s * h * ft
-    c2 = I.CONFIGS[2]["name"]
-    rows.append(Row("mlp_fwd", c2, lambda: T.tp_mlp_fwd(T.TP_ACT_GELU, BF, s, h, ft, X, W1, W2, Z, H, Y),
+    name = I.CONFIGS[cfg]["name"]
+    rows.append(Row(f"mlp_fwd_{tag}", name, lambda: T.tp_mlp_fwd(T.TP_ACT_GELU, BF, s, h, ft, X, W1, W2, Z, H, Y),
                     flops=2 * gf))
-    rows.append(Row("mlp_bwd", c2, lambda: T.tp_mlp_bwd(T.TP_ACT_GELU, BF, s, h, ft, X, W1, W2, Z, H, dY,
-                                                        dX, dW1, dW2, ws, nb), flops=4 * gf))
+    rows.append(Row(f"mlp_bwd_{tag}", name, lambda: T.tp_mlp_bwd(T.TP_ACT_GELU, BF, s, h, ft, X, W1, W2, Z, H, dY,
+                                                                 dX, dW1, dW2, ws, nb), flops=4 * gf))
     return rows
 
 
@@ -315,47 +326,176 @@ def vocab_rows(torch, up, bf, I, T):
     return rows
 
 
+def progress(msg: str) -> None:
+    """One line on stderr per finished stage (the JSON result goes to stdout)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _grow(run, work, lo, hi, budget):
+    """Time run(R) for R = lo, 2 lo, ... (at most hi) until one call takes at
+    least budget / 2 seconds; at R = hi whole calls repeat until they do.
+    Returns (rate, R, seconds, calls) of the last timing, rate = calls *
+    work(R) / seconds."""
+    R = lo
+    while True:
+        t0 = time.perf_counter()
+        run(R)
+        el = time.perf_counter() - t0
+        if el >= budget / 2:
+            return work(R) / el, R, el, 1
+        if R >= hi:
+            break
+        R = min(hi, R * 2)
+    calls = 1
+    while el < budget / 2:
+        run(R)
+        calls += 1
+        el = time.perf_counter() - t0
+    return calls * work(R) / el, R, el, calls
+
+
 def cpu_baseline(seconds: float):
-    """The fp64 oracle's MLP shard forward+backward on the GPT-2-small t=2 shard
-    (full shard weights).  The row count R doubles from 256 until one pass takes
-    a good fraction of `seconds`; when all 8192 rows fit, whole passes repeat
-    until `seconds` have elapsed.  Reported as TFLOP/s of the same 6-GEMM count."""
+    """The fp64 oracle, as it stands, on bounded samples of the bench's
+    workloads, on this host's cores.  The headline entry is the GPT-3-175B t=8
+    MLP shard forward+backward on the first R of its 2048 rows (full shard
+    weights; every product's work is linear in R, so the rate is that of the
+    whole workload); "rows" holds the other rows the same way: the rate of a
+    leading-row sample (labelled with its size), or of the whole input where it
+    is small (embedding gather, sequence-parallel slice)."""
     import ctypes
+
+    import numpy as np
 
     import oracle
     from megatron_tensor_layer_tp_amd import inputs as I
 
     oracle.build()
-    d = I.mlp_inputs(2, shards=[0])
-    X = I.bf16_bits_to_f64(d["X"])
-    dY = I.bf16_bits_to_f64(d["dY"])
-    W1 = I.bf16_bits_to_f64(d["W1"][0])
-    W2 = I.bf16_bits_to_f64(d["W2"][0])
-    h, ft = d["h"], d["ft"]
-
-    def one(R):
-        t0 = time.perf_counter()
-        oracle.mlp_fwd("gelu", X[:R], W1, W2)
-        oracle.mlp_bwd("gelu", X[:R], W1, W2, dY[:R])
-        return time.perf_counter() - t0
-
-    R = 256
-    el = one(R)
-    while el < seconds / 4 and R < d["s"]:
-        R = min(d["s"], R * 2)
-        el = one(R)
-    reps, total = 1, el
-    while total < seconds and R == d["s"]:
-        total += one(R)
-        reps += 1
-    flops = 6 * 2.0 * R * h * ft * reps
+    f = I.bf16_bits_to_f64
     try:
         threads = ctypes.CDLL("libgomp.so.1").omp_get_max_threads()
     except OSError:
         threads = None
-    return {"value": flops / total / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"MLP shard fwd+bwd (GeLU), {reps} pass(es) over {R} of {d['s']} rows of the "
-                      f"GPT-2-small t=2 shard, h={h}, f/t={ft}, fp64, {total:.2f} s"}
+    out = {"cpu_model": cpu_model(), "rows": {}}
+    rowb = max(1.0, seconds / 8)
+
+    # headline: GPT-3-175B t=8 MLP shard
+    d = I.mlp_inputs(3, shards=[0])
+    X, dY, W1, W2 = f(d["X"]), f(d["dY"]), f(d["W1"][0]), f(d["W2"][0])
+    s3, h3, f3 = d["s"], d["h"], d["ft"]
+    del d
+
+    def mlp_run(Xa, dYa, Wa, Wb):
+        def run(R):
+            oracle.mlp_fwd("gelu", Xa[:R], Wa, Wb)
+            oracle.mlp_bwd("gelu", Xa[:R], Wa, Wb, dYa[:R])
+        return run
+
+    rate, R, el, n = _grow(mlp_run(X, dY, W1, W2), lambda R: 12.0 * R * h3 * f3, 8, s3, seconds / 2)
+    out.update(value=rate / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
+               sample=f"MLP shard fwd+bwd (GeLU), {n} call(s) on {R} of {s3} rows of the GPT-3-175B t=8 shard (h={h3}, "
+                      f"f/t={f3}, full shard weights), fp64, {el:.2f} s; rate extrapolated linearly to all rows")
+    del X, dY, W1, W2
+
+    progress(f"cpu baseline: headline sample done ({el:.1f} s)")
+
+    def add(name, unit, rate, desc):
+        out["rows"][name] = {"value": rate, "unit": unit, "sample": desc}
+        progress(f"cpu baseline: {name} done")
+
+    d = I.mlp_inputs(2, shards=[0])
+    X, dY, W1, W2 = f(d["X"]), f(d["dY"]), f(d["W1"][0]), f(d["W2"][0])
+    rate, R, el, n = _grow(mlp_run(X, dY, W1, W2), lambda R: 12.0 * R * d["h"] * d["ft"], 64, d["s"], rowb)
+    add("mlp_gpt2", "TFLOP/s", rate / 1e12, f"fwd+bwd, {n} call(s) on {R} of {d['s']} rows, {el:.2f} s (extrapolated)")
+    del d, X, dY, W1, W2
+
+    sw = I.swiglu_inputs(4)
+    X, dY = f(sw["X"]), f(sw["dY"])
+    Wg, Wu, Wd = f(sw["Wg"][0]), f(sw["Wu"][0]), f(sw["Wd"][0])
+    h4, f4 = sw["h"], sw["ft"]
+    del sw
+
+    def sw_run(R):
+        oracle.swiglu_fwd(X[:R], Wg, Wu, Wd)
+        oracle.swiglu_bwd(X[:R], Wg, Wu, Wd, dY[:R])
+    rate, R, el, n = _grow(sw_run, lambda R: 18.0 * R * h4 * f4, 8, 8192, rowb)
+    add("swiglu", "TFLOP/s", rate / 1e12, f"fwd+bwd, {n} call(s) on {R} of 8192 rows, {el:.2f} s (extrapolated)")
+    del Wg, Wu, Wd
+
+    at = I.attn_inputs(4)
+    Wq, Wk, Wv, Wo = (f(at[n][0]) for n in ("Wq", "Wk", "Wv", "Wo"))
+    O, dQ, dK, dV = (f(at[n][0]) for n in ("O", "dQ", "dK", "dV"))
+    dq, dkv = at["dq"], at["dkv"]
+    del at
+
+    def at_run(R):
+        oracle.attn_fwd(X[:R], Wq, Wk, Wv, O[:R], Wo)
+        oracle.attn_bwd(X[:R], Wq, Wk, Wv, O[:R], Wo, dQ[:R], dK[:R], dV[:R], dY[:R])
+    rate, R, el, n = _grow(at_run, lambda R: 6.0 * R * h4 * (dq + 2 * dkv + dq), 8, 8192, rowb)
+    add("attn_proj", "TFLOP/s", rate / 1e12, f"fwd+bwd, {n} call(s) on {R} of 8192 rows, {el:.2f} s (extrapolated)")
+    del X, dY, Wq, Wk, Wv, Wo, O, dQ, dK, dV
+
+    ac = I.attn_core_inputs(4)
+    Qc, Kc, Vc = f(ac["Q"][0]), f(ac["K"][0]), f(ac["V"][0])
+    nq, nkv, sc = ac["nq"], ac["nkv"], ac["s"]
+    del ac
+
+    def core_rows(R):  # R positions spread evenly over the sequence
+        return np.linspace(0, sc - 1, R).astype(np.int64)
+
+    rate, R, el, n = _grow(lambda R: oracle.attn_core_fwd(Qc, Kc, Vc, nq, nkv, rows=core_rows(R)),
+                        lambda R: float(sum(4.0 * 128 * nq * (r + 1) for r in core_rows(R))), 8, sc, rowb)
+    add("attn_core_fwd", "TFLOP/s", rate / 1e12, f"{R} of {sc} query positions spread over the sequence, "
+        f"{el:.2f} s (causal FLOPs of those rows)")
+    del Qc, Kc, Vc
+
+    vd = I.vocab_inputs(5, with_table=True, with_logits=False)
+    Hf, Wlm = f(vd["Hf"]), f(vd["Wlm"][0])
+    Vs, h5, s5 = vd["Vs"], vd["h"], vd["s"]
+    rate, R, el, n = _grow(lambda R: oracle.lm_head(Hf[:R], Wlm), lambda R: 2.0 * R * h5 * Vs, 4, s5, rowb)
+    add("lm_head_fwd", "TFLOP/s", rate / 1e12, f"{n} call(s) on {R} of {s5} rows, {el:.2f} s (extrapolated)")
+    del Hf, Wlm
+    n_in = int(((vd["ids"] >= 0) & (vd["ids"] < Vs)).sum())
+    ids, table, tg = vd["ids"], vd["table"][0], vd["targets"]
+    del vd
+    rate, R, el, n = _grow(lambda R: oracle.embed(ids[:R], table, 0),
+                           lambda R: 2.0 * R * h5 + 2.0 * n_in * h5 * R / s5 + 8.0 * R, 1024, s5, rowb)
+    add("vocab_embed", "GB/s", rate / 1e9, f"{n} call(s) over {R} of {s5} ids, {el:.2f} s")
+    del table
+    z = I.normal_f32((s5, Vs), 0.905, 5, I.T_LOGITS, 0).astype(np.float64)
+    rate, R, el, n = _grow(lambda R: oracle.ce_stats(z[:R], tg[:R], 0), lambda R: (4.0 * Vs + 20.0) * R, 256, s5,
+                           rowb)
+    add("vocab_ce", "GB/s", rate / 1e9, f"{n} call(s) over {R} of {s5} positions of fp32 logits, {el:.2f} s")
+    m, se, _ = oracle.ce_stats(z, tg, 0)
+    g = np.full(s5, 1.0 / s5)
+    rate, R, el, n = _grow(lambda R: oracle.ce_bwd(z[:R], tg[:R], 0, m[:R], se[:R], g[:R]),
+                           lambda R: (6.0 * Vs + 20.0) * R, 256, s5, rowb)
+    add("vocab_ce_bwd", "GB/s", rate / 1e9, f"{n} call(s) over {R} of {s5} positions, {el:.2f} s")
+    del z
+
+    sp = I.sp_inputs(4)
+    y_, x_, gm, bt = f(sp["y"]), f(sp["x"]), f(sp["gamma"]), f(sp["beta"])
+    n_sp, hs = sp["n"], sp["h"]
+    mask, dz_, dun_ = sp["mask"], f(sp["dz"]), f(sp["dun"])
+    rate, R, el, n = _grow(lambda R: oracle.sp_ln_fwd(y_[:R], x_[:R], mask[:R], gm, bt, sp["p"]),
+                           lambda R: 9.0 * R * hs + 4.0 * hs + 8.0 * R, 64, n_sp, rowb)
+    add("sp_ln_fwd", "GB/s", rate / 1e9, f"{n} call(s) over {R} of {n_sp} rows x {hs}, {el:.2f} s")
+    u, zz, mu, rs = oracle.sp_ln_fwd(y_, x_, mask, gm, bt, sp["p"])
+    rate, R, el, n = _grow(lambda R: oracle.sp_ln_bwd(dz_[:R], dun_[:R], u[:R], mu[:R], rs[:R], gm, mask[:R],
+                                                      sp["p"]),
+                           lambda R: 11.0 * R * hs + 6.0 * hs + 8.0 * R, 64, n_sp, rowb)
+    add("sp_ln_bwd", "GB/s", rate / 1e9, f"{n} call(s) over {R} of {n_sp} rows x {hs}, {el:.2f} s")
+    return out
 
 
 def traffic_for(kernel_key: str):
@@ -456,6 +596,7 @@ def main():
         return
     first = "lm_head_fwd" if args.only in ("vocab_ce", "vocab_ce_bwd") else args.only
     rows = build_rows(torch, args.rows, first)
+    progress(f"inputs resident, {len(rows)} rows")
     if args.only:
         keep = [r for r in rows if r.name == args.only]
         if not keep:
@@ -471,6 +612,7 @@ def main():
         for r in rows:
             r.run(torch, False)
     torch.cuda.synchronize()
+    progress("warm-up done")
     with GpuSampler() as sampler:
         t0 = time.perf_counter()
         for _ in range(args.steps):
@@ -478,6 +620,7 @@ def main():
                 r.run(torch, True)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+    progress(f"timed {args.steps} steps in {wall:.2f} s")
 
     by = {r.name: r for r in rows}
     if args.only:
@@ -487,9 +630,16 @@ def main():
                           "tflops": r.flops / (ms * 1e-3) / 1e12 if r.flops else None,
                           "gbs": r.bytes / (ms * 1e-3) / 1e9 if r.bytes else None}))
         return
-    mlp_ms = by["mlp_fwd"].ms() + by["mlp_bwd"].ms()
-    mlp_flops = by["mlp_fwd"].flops + by["mlp_bwd"].flops
-    value = mlp_flops / (mlp_ms * 1e-3) / 1e12
+    def mlp_rate(tag):
+        ms = by[f"mlp_fwd_{tag}"].ms() + by[f"mlp_bwd_{tag}"].ms()
+        return (by[f"mlp_fwd_{tag}"].flops + by[f"mlp_bwd_{tag}"].flops) / (ms * 1e-3) / 1e12
+
+    value = mlp_rate("gpt3")
+    other_mlp = {"gpt2-small-gelu-mlp-t2 (s=8192, h=768, f/t=1536) fwd+bwd TFLOP/s": round(mlp_rate("gpt2"), 2)}
+    if "swiglu_fwd" in by:
+        sw_ms = by["swiglu_fwd"].ms() + by["swiglu_bwd"].ms()
+        other_mlp["llama3-70b-swiglu-t8 (s=8192, h=8192, f/t=3584) fwd+bwd TFLOP/s"] = round(
+            (by["swiglu_fwd"].flops + by["swiglu_bwd"].flops) / (sw_ms * 1e-3) / 1e12, 2)
     out_rows = {}
     for r in rows:
         ms = r.ms()
@@ -516,11 +666,14 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,sigma) bf16 inputs, random-init weights)",
-        "config": {"workload": "gpt2-small-gelu-mlp-t2: s=8192 (b=8 x 1024), h=768, f/t=1536, bf16",
+        "config": {"workload": "gpt3-175b-gelu-mlp-t8: s=2048 (b=1), h=12288, f/t=6144, GeLU, bf16",
                    "frac_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4),
-                   "step_rows": "mlp fwd+bwd (this workload); swiglu + attention projections fwd+bwd "
-                                "(llama3-70b t=8, s=8192); lm head + vocab CE + embedding "
-                                "(V=128256 t=8, s=8192)" if args.rows == "all" else "mlp fwd+bwd only"},
+                   "other_mlp_workloads": other_mlp,
+                   "step_rows": "mlp fwd+bwd (this workload, and gpt2-small t=2); swiglu + attention "
+                                "projections + attention core fwd+bwd + sequence-parallel region "
+                                "(llama3-70b t=8, s=8192); lm head + vocab CE (+ backward) + fused "
+                                "lm head/CE + embedding (V=128256 t=8, s=8192)"
+                                if args.rows == "all" else "mlp fwd+bwd only"},
         "rows": out_rows,
         "gpu_during_steps": sampler.summary(),
     }
@@ -540,7 +693,7 @@ def main():
                               "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                               "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": traffic_for("vocab_ce")}
     else:
-        r = by["mlp_bwd"]
+        r = by["mlp_bwd_gpt3"]
         ach = r.flops / (r.ms() * 1e-3) / 1e12
         res["roofline"] = {"kernel": "gemm_dma kernels (tp_mlp_bwd, 4 GEMMs)", "bound": "mfma",
                            "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

@@ -251,12 +251,23 @@ def vocab_inputs(cfg_id: int = 5, shards=(0,), s=None, h=None, V=None, t=None,
     return out
 
 
-def sample_rows(n: int, k: int, config: int, salt: int = 0) -> np.ndarray:
-    """k distinct sorted indices in [0, n) (all of them when k >= n), seeded."""
+def sample_rows(n: int, k: int, config: int, salt: int = 0, stratum: int = 64) -> np.ndarray:
+    """Seeded, sorted, distinct indices in [0, n) for sampled parity checks.
+
+    Stratified: one index drawn uniformly inside every run of ``stratum``
+    consecutive indices (so every 64-row strip -- each wave's slice of a 128-
+    or 256-row tile, each 128-row query block -- holds at least one), the
+    first and the last index (edge tiles), then further distinct random
+    indices until there are at least ``k``.  All of [0, n) when k >= n.
+    """
     if k >= n:
         return np.arange(n, dtype=np.int64)
     g = _rng(config, 1000 + salt, 0)
-    idx = g.choice(n, size=k, replace=False)
-    # always include the first and the last index: they sit in edge tiles
-    idx[0], idx[-1] = 0, n - 1
-    return np.unique(idx).astype(np.int64)
+    starts = np.arange(0, n, stratum, dtype=np.int64)
+    widths = np.minimum(stratum, n - starts)
+    picked = set((starts + (g.random(starts.shape[0]) * widths).astype(np.int64)).tolist())
+    picked.update((0, n - 1))
+    if len(picked) < k:
+        rest = np.setdiff1d(np.arange(n, dtype=np.int64), np.fromiter(picked, dtype=np.int64))
+        picked.update(g.choice(rest, size=k - len(picked), replace=False).tolist())
+    return np.array(sorted(picked), dtype=np.int64)

@@ -64,3 +64,42 @@ def workspace(nbytes: int):
     if nbytes == 0:
         return None, 0
     return torch.empty(nbytes, dtype=torch.uint8, device=DEV), nbytes
+
+
+# Element-wise bound for bf16 outputs, next to the relative Frobenius bar:
+#   |got - want| <= 2^-7 |want| + 2^-5 rms(want)   (rms over the compared entries)
+# The first term covers the output's own round-to-nearest-even (at most 2^-8
+# relative) with a factor 2 to spare; the second covers the bf16 roundings of
+# the intermediates a product consumes (Z, H, A, dZ, dG, P): each is at most
+# 2^-8 relative, so the error they carry into an output has a standard
+# deviation near 0.6 * 2^-8 rms per rounded operand -- the bound sits at more
+# than 6 of those standard deviations for two chained roundings.  A wrong or
+# skipped element is off by the order of rms(want) and fails it.
+BF16_REL = 2.0 ** -7
+BF16_RMS = 2.0 ** -5
+
+
+def elem_bound(got: np.ndarray, want: np.ndarray, name: str, rel: float = BF16_REL, rms_frac: float = BF16_RMS):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, (name, got.shape, want.shape)
+    if want.size == 0:
+        return
+    assert np.all(np.isfinite(got)), f"{name}: non-finite values in the GPU result"
+    rms = float(np.sqrt(np.mean(want * want)))
+    err = np.abs(got - want)
+    lim = rel * np.abs(want) + rms_frac * rms
+    bad = np.argwhere(err > lim)
+    assert bad.size == 0, (f"{name}: {bad.shape[0]} of {want.size} entries outside |err| <= {rel:.3g}|want| + "
+                           f"{rms_frac:.3g} rms; first at {tuple(bad[0])}: got {got[tuple(bad[0])]!r}, "
+                           f"want {want[tuple(bad[0])]!r}, rms {rms:.3g}")
+
+
+def check_bf16(got: np.ndarray, want: np.ndarray, name: str, tol: float = 5e-3, rel: float = BF16_REL,
+               rms_frac: float = BF16_RMS) -> float:
+    """The parity bar for a bf16 output (or a sample of one): relative
+    Frobenius error <= tol over the whole tensor and the element-wise bound."""
+    err = rel_fro(got, want)
+    assert err <= tol, f"{name}: relative Frobenius error {err:.3e} > {tol}"
+    elem_bound(got, want, name, rel, rms_frac)
+    return err

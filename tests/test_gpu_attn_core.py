@@ -2,17 +2,19 @@
 "7.3 模型并行与张量并行" §7.3.4: the card's query heads share its key/value
 head) against the fp64 oracle.
 
-  * O (bf16) within 5e-3 relative Frobenius of the oracle per head, at small,
-    ragged (s not a multiple of the 128-row query block or the 64-key tile)
-    and grouped (nq / nkv = 1, 2, 4, 8) sizes, and on sampled rows of the
-    Llama-3-70B t=8 shard (s = 8192, 8 query heads, 1 KV head);
+  * O (bf16) within 5e-3 relative Frobenius of the oracle per head and within
+    the element-wise bound of gpu_util.elem_bound, at small, ragged (s not a
+    multiple of the 128-row query block or the 64-key tile) and grouped
+    (nq / nkv = 1, 2, 4, 8) sizes, and on stratified sampled rows (one in every
+    64-row half of each query block) of the Llama-3-70B t=8 shard (s = 8192,
+    8 query heads, 1 KV head);
   * the log-sum-exp of each row's scores within 1e-4 absolute;
   * run twice, bit-identical.
 """
 import numpy as np
 import pytest
 
-from gpu_util import dev, fill_garbage, host, host_f64, need_gpu, rel_fro, torch
+from gpu_util import check_bf16, dev, fill_garbage, host, host_f64, need_gpu, torch
 from megatron_tensor_layer_tp_amd import inputs as I
 from megatron_tensor_layer_tp_amd import tpshard as T
 
@@ -41,8 +43,7 @@ def check(got_O, got_lse, want_O, want_lse, nq, rows=None):
     if rows is not None:
         O, lse = O[rows], lse[:, rows]
     for j in range(nq):
-        err = rel_fro(O[:, j * D:(j + 1) * D], want_O[:, j * D:(j + 1) * D])
-        assert err <= 5e-3, (j, err)
+        check_bf16(O[:, j * D:(j + 1) * D], want_O[:, j * D:(j + 1) * D], f"O head {j}")
     assert np.abs(lse - want_lse).max() <= 1e-4
 
 
@@ -63,7 +64,7 @@ def test_core_llama3_shard_sampled(oracle_mod):
     Q, K, V = d["Q"][0], d["K"][0], d["V"][0]
     nq, nkv, s = d["nq"], d["nkv"], d["s"]
     O, lse = run_core(Q, K, V, nq, nkv)
-    rows = I.sample_rows(s, 48, 4, 31)
+    rows = I.sample_rows(s, 64, 4, 31)
     wO, wl = oracle_mod.attn_core_fwd(*(I.bf16_bits_to_f64(a) for a in (Q, K, V)), nq, nkv, rows=rows)
     check(O, lse, wO, wl, nq, rows)
     O2, lse2 = run_core(Q, K, V, nq, nkv)

@@ -128,7 +128,7 @@ def test_fused_vocab_shard(oracle_mod):
     Hf, W, tgt = d["Hf"], d["Wlm"][0], d["targets"]
     got = run_fused(Hf, W, tgt, 0)
     check_vs_unfused(got, run_unfused(Hf, W, tgt, 0))
-    rows = I.sample_rows(d["s"], 32, 5, 22)
+    rows = I.sample_rows(d["s"], 64, 5, 22)
     # make sure some sampled targets fall inside the shard
     z = oracle_mod.lm_head_rows(I.bf16_bits_to_f64(Hf), I.bf16_bits_to_f64(W), rows)
     want = oracle_mod.ce_stats(z, tgt[rows], 0)

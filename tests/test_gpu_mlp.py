@@ -9,9 +9,10 @@ Exact cases (bit for bit):
     is the bf16 store of each output and of the saved Z / H / dZ, and the GPU
     must reproduce the oracle's values rounded at exactly those points.
 Floating-point cases: relative Frobenius error <= 5e-3 per output against the
-fp64 oracle (no intermediate rounding on the oracle side), on full outputs for
-small sizes and on sampled rows / columns at the GPT-2-small and GPT-3-175B
-shard sizes.
+fp64 oracle (no intermediate rounding on the oracle side) plus the element-wise
+bound of gpu_util.elem_bound, on full outputs for small sizes and on
+stratified sampled rows / columns (one in every 64-row or 64-column strip, at
+least 64) at the GPT-2-small and GPT-3-175B shard sizes.
 """
 import json
 import os
@@ -19,7 +20,7 @@ import os
 import numpy as np
 import pytest
 
-from gpu_util import (DEV, dev, empty_like_dt, fill_garbage, host, host_f64, need_gpu, rel_fro,
+from gpu_util import (DEV, check_bf16, dev, empty_like_dt, fill_garbage, host, host_f64, need_gpu,
                       torch, workspace)
 from megatron_tensor_layer_tp_amd import inputs as I
 from megatron_tensor_layer_tp_amd import tpshard as T
@@ -151,9 +152,7 @@ def check_close(got_t, want, name, tol=TOL, rows=None, cols=None):
         got = got[rows]
     if cols is not None:
         got = got[:, cols]
-    err = rel_fro(got, want)
-    assert err <= tol, f"{name}: relative Frobenius error {err:.3e} > {tol}"
-    return err
+    return check_bf16(got, want, name, tol=tol)
 
 
 @pytest.mark.parametrize("s,h,ft", [(300, 200, 136), (520, 264, 392), (256, 256, 512)])
@@ -201,6 +200,5 @@ def test_gpt2_small_shard_sampled(oracle_mod):
         assert torch.equal(o[k], o2[k]), k
 
 
-@pytest.mark.slow
 def test_gpt3_shard_sampled(oracle_mod):
-    _sampled_config(oracle_mod, 3, 32, 32)
+    _sampled_config(oracle_mod, 3, 64, 64)

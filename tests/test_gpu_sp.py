@@ -3,7 +3,8 @@
 card's s/t positions) against the fp64 oracle.
 
   * u within one bf16 rounding of the oracle's value; z, dx, dy, dgamma and
-    dbeta within 5e-3 relative Frobenius; mean within 1e-4 and rstd within 1e-4
+    dbeta within 5e-3 relative Frobenius and the element-wise bound of
+    gpu_util.elem_bound; mean within 1e-4 and rstd within 1e-4
     relative -- at the Llama-3-70B t=8 slice (1024 x 8192), at small and
     ragged widths (16-byte and element-wise paths), with and without dropout,
     and at a width that needs two register passes per row (12000);
@@ -14,7 +15,7 @@ card's s/t positions) against the fp64 oracle.
 import numpy as np
 import pytest
 
-from gpu_util import dev, fill_garbage, host, host_f64, need_gpu, rel_fro, torch
+from gpu_util import check_bf16, dev, fill_garbage, host, host_f64, need_gpu, rel_fro, torch
 from megatron_tensor_layer_tp_amd import inputs as I
 from megatron_tensor_layer_tp_amd import tpshard as T
 
@@ -69,8 +70,7 @@ def check(got, want, d, rows=None):
     mag = np.abs(I.bf16_bits_to_f64(d["x"][sl])) + np.abs(I.bf16_bits_to_f64(d["y"][sl])) / (1 - d["p"])
     assert np.all(np.abs(u - want["u"]) <= 2.0 ** -8 * np.abs(want["u"]) + 2.0 ** -22 * mag)
     for k in ("z", "dx", "dy", "dg", "db"):
-        err = rel_fro(host_f64(got[k]), want[k])
-        assert err <= 5e-3, (k, err)
+        check_bf16(host_f64(got[k]), want[k], k)
     assert np.abs(host(got["mean"]) - want["mean"]).max() <= 1e-4
     assert np.max(np.abs(host(got["rstd"]) - want["rstd"]) / want["rstd"]) <= 1e-4
 

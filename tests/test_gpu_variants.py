@@ -4,15 +4,17 @@ workgroups per CU) on the same products, each checked against the fp64 oracle.
 The planner normally picks one variant per product from its cost model, so most
 variants would only run at the sizes where they win; TP_GEMM_VARIANT restricts
 every product that has the variant built to it (split-K and pairing still
-planned), which puts each variant through the MLP (integer inputs, bit-exact),
-SwiGLU, attention-projection and fused LM-head + CE paths at ragged sizes."""
+planned), which puts each variant through the MLP, the attention projections
+and SwiGLU's gate/up pass with integer inputs (bit-exact), the SwiGLU and
+attention-projection paths with float inputs, and the fused LM-head + CE path,
+at ragged sizes."""
 import numpy as np
 import pytest
 
 from gpu_util import need_gpu
 from megatron_tensor_layer_tp_amd import inputs as I
 from megatron_tensor_layer_tp_amd import tpshard as T
-from test_gpu_layer import bf, close, run_attn, run_swiglu
+from test_gpu_layer import attn_integer_case, bf, close, run_attn, run_swiglu, swiglu_integer_case
 from test_gpu_lm_ce import check_vs_oracle, run_fused
 from test_gpu_mlp import integer_exact_case
 
@@ -37,6 +39,15 @@ def variant(request, monkeypatch):
 @pytest.mark.parametrize("s,h,ft", [(520, 200, 1000), (2056, 136, 392)])
 def test_mlp_integer_exact(oracle_mod, variant, s, h, ft):
     integer_exact_case(oracle_mod, s, h, ft)
+
+
+@pytest.mark.parametrize("s,h,dq,dkv", [(520, 264, 256, 32), (2056, 136, 392, 136)])
+def test_attn_proj_integer_exact(oracle_mod, variant, s, h, dq, dkv):
+    attn_integer_case(oracle_mod, s, h, dq, dkv)
+
+
+def test_swiglu_gate_up_integer_exact(oracle_mod, variant):
+    swiglu_integer_case(oracle_mod, 520, 264, 392)
 
 
 def test_swiglu(oracle_mod, variant):

@@ -1,5 +1,6 @@
 """The seeded input generator: bf16 rounding, determinism and shard keys."""
 import numpy as np
+import pytest
 import torch
 
 from megatron_tensor_layer_tp_amd import inputs as I
@@ -36,3 +37,16 @@ def test_sample_rows_include_edges():
     r = I.sample_rows(1000, 64, 3)
     assert r[0] == 0 and r[-1] == 999 and len(set(r)) == len(r) and np.all(np.diff(r) > 0)
     assert np.array_equal(I.sample_rows(5, 64, 3), np.arange(5))
+
+
+@pytest.mark.parametrize("n,k,stratum", [(8192, 64, 64), (8192, 64, 128), (6144, 64, 64), (16032, 64, 64),
+                                         (1024, 64, 64), (128, 64, 64), (100, 64, 32), (8200, 64, 64)])
+def test_sample_rows_stratified(n, k, stratum):
+    """Every run of `stratum` consecutive indices (every tile strip) holds a
+    sampled index, there are at least k of them, and the draw is seeded."""
+    r = I.sample_rows(n, k, 4, 7, stratum=stratum)
+    assert len(r) >= min(n, k) and r[0] == 0 and r[-1] == n - 1 and np.all(np.diff(r) > 0)
+    assert r.min() >= 0 and r.max() < n
+    for s0 in range(0, n, stratum):
+        assert np.any((r >= s0) & (r < s0 + stratum)), s0
+    assert np.array_equal(r, I.sample_rows(n, k, 4, 7, stratum=stratum))
