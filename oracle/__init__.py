@@ -65,6 +65,8 @@ def _L():
                                      _d, _d, _d, _d]
         lib.or_attn_fwd.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, _d, _d, _d, _i64, ctypes.c_void_p,
                                     _d, _d]
+        lib.or_attn_bwd.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, _d, _d, _d, _d, _i64, ctypes.c_void_p,
+                                    _i64, ctypes.c_void_p, _d, _d, _d]
         lib.or_embed_u16.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_void_p,
                                      ctypes.c_void_p, ctypes.c_void_p]
         lib.or_embed_u32.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_void_p,
@@ -401,6 +403,29 @@ def attn_core_fwd(Q, K, V, nq: int, nkv: int, causal: bool = True, rows=None):
         _L().or_attn_fwd(s, nq, nkv, d, int(bool(causal)), _p(Q), _p(K), _p(V), nr, rows.ctypes.data,
                          _p(O), _p(lse))
     return O, lse
+
+
+def attn_core_bwd(Q, K, V, dO, nq: int, nkv: int, causal: bool = True, rows=None, cols=None):
+    """Gradients of attn_core_fwd's O with respect to Q, K, V for the incoming
+    gradient dO [s, nq*d]: with P the attention weights of head j (KV head g),
+    dP = dO_j V_g^T, dS = P * (dP - rowsum(P * dP)), dQ_j = dS K_g / sqrt(d),
+    dK_g = sum over the group's heads of dS^T Q_j / sqrt(d), dV_g = sum over
+    the group's heads of P^T dO_j.  Returns dQ at positions ``rows`` [nr, nq*d]
+    and dK, dV at key positions ``cols`` [nc, nkv*d] (all positions when None)."""
+    Q, K, V, dO = _f64(Q), _f64(K), _f64(V), _f64(dO)
+    s = Q.shape[0]
+    d = Q.shape[1] // nq
+    assert Q.shape == dO.shape and K.shape == (s, nkv * d) and V.shape == K.shape and nq % nkv == 0
+    rows = np.arange(s, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    cols = np.arange(s, dtype=np.int64) if cols is None else np.ascontiguousarray(cols, dtype=np.int64)
+    nr, nc = rows.shape[0], cols.shape[0]
+    dQ = np.zeros((nr, nq * d))
+    dK = np.zeros((nc, nkv * d))
+    dV = np.zeros((nc, nkv * d))
+    if s and d and nq:
+        _L().or_attn_bwd(s, nq, nkv, d, int(bool(causal)), _p(Q), _p(K), _p(V), _p(dO), nr, rows.ctypes.data,
+                         nc, cols.ctypes.data, _p(dQ), _p(dK), _p(dV))
+    return dQ, dK, dV
 
 
 # ---------------------------------------------------------------------------

@@ -337,3 +337,109 @@ void or_sp_ln_bwd(int64_t n, int64_t h, double p, const double *dz, const double
         }
     }
 }
+
+/* ---------------------------------------------------------------------- */
+/* attention core on the shard's heads: backward                           */
+/* ---------------------------------------------------------------------- */
+
+/* Gradients of or_attn_fwd's O with respect to Q, K and V, given dO, the
+ * gradient arriving at O (same layout as O).  Differentiating
+ * O_j[r] = sum_c P[r][c] V_g[c] with P[r][.] = softmax_c(S[r][.]) and
+ * S[r][c] = Q_j[r] . K_g[c] / sqrt(d), for each head j (KV head g = j / (nq/nkv)):
+ *   dP[r][c] = dO_j[r] . V_g[c]
+ *   D[r]     = sum_c P[r][c] dP[r][c]            (softmax Jacobian: dS = P (dP - D))
+ *   dS[r][c] = P[r][c] (dP[r][c] - D[r])
+ *   dQ_j[r]  = sum_c dS[r][c] K_g[c] / sqrt(d)
+ *   dK_g[c]  = sum over the heads j of group g, then over r, of dS[r][c] Q_j[r] / sqrt(d)
+ *   dV_g[c]  = sum over the heads j of group g, then over r, of P[r][c] dO_j[r]
+ * with c <= r when causal.  The query heads of a group share their key/value
+ * head, so its gradient is the sum of theirs (heads in increasing order, rows
+ * in increasing order).
+ * Outputs are taken at nr sampled positions rows[] (dQ [nr][nq*d]) and nc
+ * sampled key positions cols[] (dK, dV [nc][nkv*d]); all positions give the
+ * whole backward.  P and D are first evaluated for every (head, position),
+ * since a key's gradient needs every later query's softmax. */
+void or_attn_bwd(int64_t s, int64_t nq, int64_t nkv, int64_t d, int causal, const double *Q,
+                 const double *K, const double *V, const double *dO, int64_t nr, const int64_t *rows,
+                 int64_t nc, const int64_t *cols, double *dQ, double *dK, double *dV)
+{
+    const int64_t grp = nq / nkv, lq = nq * d, lk = nkv * d;
+    const double scale = 1.0 / sqrt((double)d);
+    double *lse = (double *)malloc((size_t)(nq * s > 0 ? nq * s : 1) * sizeof(double));
+    double *Dv = (double *)malloc((size_t)(nq * s > 0 ? nq * s : 1) * sizeof(double));
+
+    /* log-sum-exp of every score row and D of every (head, position) */
+    #pragma omp parallel for schedule(dynamic) collapse(2)
+    for (int64_t j = 0; j < nq; ++j) {
+        for (int64_t r = 0; r < s; ++r) {
+            const int64_t g = j / grp, n = causal ? r + 1 : s;
+            double *S = (double *)malloc((size_t)n * sizeof(double));
+            double m = -INFINITY;
+            for (int64_t c = 0; c < n; ++c) {
+                double acc = 0.0;
+                for (int64_t k = 0; k < d; ++k) acc += Q[r * lq + j * d + k] * K[c * lk + g * d + k];
+                S[c] = acc * scale;
+                if (S[c] > m) m = S[c];
+            }
+            double sum = 0.0;
+            for (int64_t c = 0; c < n; ++c) sum += exp(S[c] - m);
+            const double L = m + log(sum);
+            double Dr = 0.0;
+            for (int64_t c = 0; c < n; ++c) {
+                double dp = 0.0;
+                for (int64_t k = 0; k < d; ++k) dp += dO[r * lq + j * d + k] * V[c * lk + g * d + k];
+                Dr += exp(S[c] - L) * dp;
+            }
+            lse[j * s + r] = L;
+            Dv[j * s + r] = Dr;
+            free(S);
+        }
+    }
+
+    /* dQ at the sampled positions */
+    #pragma omp parallel for schedule(dynamic) collapse(2)
+    for (int64_t j = 0; j < nq; ++j) {
+        for (int64_t i = 0; i < nr; ++i) {
+            const int64_t r = rows[i], g = j / grp, n = causal ? r + 1 : s;
+            double *out = dQ + i * lq + j * d;
+            for (int64_t k = 0; k < d; ++k) out[k] = 0.0;
+            for (int64_t c = 0; c < n; ++c) {
+                double sc = 0.0, dp = 0.0;
+                for (int64_t k = 0; k < d; ++k) {
+                    sc += Q[r * lq + j * d + k] * K[c * lk + g * d + k];
+                    dp += dO[r * lq + j * d + k] * V[c * lk + g * d + k];
+                }
+                const double p = exp(sc * scale - lse[j * s + r]);
+                const double ds = p * (dp - Dv[j * s + r]);
+                for (int64_t k = 0; k < d; ++k) out[k] += ds * K[c * lk + g * d + k] * scale;
+            }
+        }
+    }
+
+    /* dK and dV at the sampled key positions */
+    #pragma omp parallel for schedule(dynamic) collapse(2)
+    for (int64_t g = 0; g < nkv; ++g) {
+        for (int64_t i = 0; i < nc; ++i) {
+            const int64_t c = cols[i];
+            double *ok = dK + i * lk + g * d, *ov = dV + i * lk + g * d;
+            for (int64_t k = 0; k < d; ++k) ok[k] = ov[k] = 0.0;
+            for (int64_t j = g * grp; j < (g + 1) * grp; ++j) {
+                for (int64_t r = causal ? c : 0; r < s; ++r) {
+                    double sc = 0.0, dp = 0.0;
+                    for (int64_t k = 0; k < d; ++k) {
+                        sc += Q[r * lq + j * d + k] * K[c * lk + g * d + k];
+                        dp += dO[r * lq + j * d + k] * V[c * lk + g * d + k];
+                    }
+                    const double p = exp(sc * scale - lse[j * s + r]);
+                    const double ds = p * (dp - Dv[j * s + r]);
+                    for (int64_t k = 0; k < d; ++k) {
+                        ok[k] += ds * Q[r * lq + j * d + k] * scale;
+                        ov[k] += p * dO[r * lq + j * d + k];
+                    }
+                }
+            }
+        }
+    }
+    free(lse);
+    free(Dv);
+}

@@ -110,3 +110,119 @@ def test_brute_force_tiny(oracle_mod):
             for k in range(d):
                 want = sum(math.exp(sc[c]) / z * V[c, k] for c in range(r + 1))
                 assert abs(O[r, j * d + k] - want) <= 1e-13
+
+
+# ---------------------------------------------------------------- backward
+# Pins of attn_core_bwd (dO -> dQ, dK, dV of the same attention):
+# - torch fp64 autograd through scaled_dot_product_attention, the key/value
+#   heads repeated for the grouped query heads (autograd then sums a shared
+#   head's gradient over its group);
+# - central differences of L = sum(dO * O) with the oracle's own forward;
+# - grouping: the grouped dK, dV equal the per-head gradients of plain
+#   multi-head attention on repeated heads, summed over each group;
+# - closed form of uniform attention (all keys zero): dQ = 0,
+#   dV[c] = sum_j sum_{r>=c} dO_j[r] / (r+1), and
+#   dK[c] = sum_j sum_{r>=c} (dO_j[r].V[c] - dO_j[r].mean_{c'<=r} V[c']) Q_j[r] / ((r+1) sqrt d);
+# - shifting every key by one vector leaves all three unchanged (the softmax
+#   is shift invariant per row and each dS row sums to zero);
+# - sampled positions equal the full computation, bit for bit.
+def _torch_bwd(Q, K, V, dO, nq, nkv, causal):
+    s = Q.shape[0]
+    d = Q.shape[1] // nq
+    q = torch.tensor(Q).reshape(s, nq, d).transpose(0, 1).requires_grad_(True)
+    k = torch.tensor(K).reshape(s, nkv, d).transpose(0, 1).requires_grad_(True)
+    v = torch.tensor(V).reshape(s, nkv, d).transpose(0, 1).requires_grad_(True)
+    kr = k.repeat_interleave(nq // nkv, dim=0)
+    vr = v.repeat_interleave(nq // nkv, dim=0)
+    o = torch.nn.functional.scaled_dot_product_attention(q, kr, vr, is_causal=causal)
+    o.backward(torch.tensor(dO).reshape(s, nq, d).transpose(0, 1))
+    f = lambda t, n: t.grad.transpose(0, 1).reshape(s, n * d).numpy()  # noqa: E731
+    return f(q, nq), f(k, nkv), f(v, nkv)
+
+
+@pytest.mark.parametrize("s,nq,nkv,d,causal", [(33, 8, 1, 16, True), (20, 4, 2, 8, True), (17, 2, 2, 32, False),
+                                               (64, 8, 1, 128, True), (9, 4, 4, 8, False)])
+def test_bwd_matches_torch_autograd(oracle_mod, s, nq, nkv, d, causal):
+    Q, K, V = _rand(s + 3 * d, s, nq, nkv, d)
+    dO = np.random.default_rng(s + 7).standard_normal((s, nq * d))
+    dQ, dK, dV = oracle_mod.attn_core_bwd(Q, K, V, dO, nq, nkv, causal)
+    wq, wk, wv = _torch_bwd(Q, K, V, dO, nq, nkv, causal)
+    for got, want in ((dQ, wq), (dK, wk), (dV, wv)):
+        np.testing.assert_allclose(got, want, rtol=1e-10, atol=1e-11)
+
+
+def test_bwd_central_differences(oracle_mod):
+    s, nq, nkv, d = 12, 4, 2, 8
+    Q, K, V = _rand(21, s, nq, nkv, d)
+    dO = np.random.default_rng(22).standard_normal((s, nq * d))
+    dQ, dK, dV = oracle_mod.attn_core_bwd(Q, K, V, dO, nq, nkv)
+    loss = lambda q, k, v: float(np.sum(dO * oracle_mod.attn_core_fwd(q, k, v, nq, nkv)[0]))  # noqa: E731
+    h = 1e-5
+    g = np.random.default_rng(23)
+    for which, grad in ((0, dQ), (1, dK), (2, dV)):
+        for _ in range(6):
+            r, c = int(g.integers(s)), int(g.integers(grad.shape[1]))
+            args_p = [Q.copy(), K.copy(), V.copy()]
+            args_m = [Q.copy(), K.copy(), V.copy()]
+            args_p[which][r, c] += h
+            args_m[which][r, c] -= h
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * h)
+            assert abs(fd - grad[r, c]) <= 1e-7 * max(1.0, abs(fd)), (which, r, c, fd, grad[r, c])
+
+
+def test_bwd_grouping_sums_repeated_heads(oracle_mod):
+    s, nq, nkv, d = 19, 8, 2, 8
+    Q, K, V = _rand(24, s, nq, nkv, d)
+    dO = np.random.default_rng(25).standard_normal((s, nq * d))
+    dQ, dK, dV = oracle_mod.attn_core_bwd(Q, K, V, dO, nq, nkv)
+    grp = nq // nkv
+    rep = lambda X: np.concatenate([X[:, (j // grp) * d:(j // grp + 1) * d] for j in range(nq)], axis=1)  # noqa: E731
+    dQ2, dK2, dV2 = oracle_mod.attn_core_bwd(Q, rep(K), rep(V), dO, nq, nq)
+    np.testing.assert_allclose(dQ, dQ2, rtol=1e-13, atol=1e-14)
+    for g in range(nkv):
+        heads = range(g * grp, (g + 1) * grp)
+        np.testing.assert_allclose(dK[:, g * d:(g + 1) * d], sum(dK2[:, j * d:(j + 1) * d] for j in heads),
+                                   rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(dV[:, g * d:(g + 1) * d], sum(dV2[:, j * d:(j + 1) * d] for j in heads),
+                                   rtol=1e-12, atol=1e-13)
+
+
+def test_bwd_uniform_attention_closed_form(oracle_mod):
+    s, nq, nkv, d = 14, 2, 1, 8
+    Q, _, V = _rand(26, s, nq, nkv, d)
+    K = np.zeros((s, nkv * d))
+    dO = np.random.default_rng(27).standard_normal((s, nq * d))
+    dQ, dK, dV = oracle_mod.attn_core_bwd(Q, K, V, dO, nq, nkv)
+    assert np.array_equal(dQ, np.zeros_like(dQ))
+    mean = np.cumsum(V, axis=0) / np.arange(1, s + 1)[:, None]
+    wv = np.zeros((s, d))
+    wk = np.zeros((s, d))
+    for j in range(nq):
+        dOj, Qj = dO[:, j * d:(j + 1) * d], Q[:, j * d:(j + 1) * d]
+        for c in range(s):
+            for r in range(c, s):
+                wv[c] += dOj[r] / (r + 1)
+                wk[c] += (dOj[r] @ V[c] - dOj[r] @ mean[r]) * Qj[r] / ((r + 1) * math.sqrt(d))
+    np.testing.assert_allclose(dV, wv, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dK, wk, rtol=1e-10, atol=1e-12)
+
+
+def test_bwd_key_shift_invariance(oracle_mod):
+    s, nq, nkv, d = 21, 4, 1, 16
+    Q, K, V = _rand(28, s, nq, nkv, d)
+    dO = np.random.default_rng(29).standard_normal((s, nq * d))
+    a = np.random.default_rng(30).standard_normal(d)
+    base = oracle_mod.attn_core_bwd(Q, K, V, dO, nq, nkv)
+    shifted = oracle_mod.attn_core_bwd(Q, K + a[None, :], V, dO, nq, nkv)
+    for x, y in zip(base, shifted):
+        np.testing.assert_allclose(x, y, rtol=1e-9, atol=1e-11)
+
+
+def test_bwd_sampled_equals_full(oracle_mod):
+    s, nq, nkv, d = 40, 4, 2, 16
+    Q, K, V = _rand(31, s, nq, nkv, d)
+    dO = np.random.default_rng(32).standard_normal((s, nq * d))
+    dQ, dK, dV = oracle_mod.attn_core_bwd(Q, K, V, dO, nq, nkv)
+    rows, cols = np.array([0, 7, 39, 13]), np.array([39, 0, 5])
+    sq, sk, sv = oracle_mod.attn_core_bwd(Q, K, V, dO, nq, nkv, rows=rows, cols=cols)
+    assert np.array_equal(sq, dQ[rows]) and np.array_equal(sk, dK[cols]) and np.array_equal(sv, dV[cols])
