@@ -190,8 +190,8 @@ def build_rows(torch, which, only=None):
         progress(f"inputs: {rows[-1].config} ready")
     if which == "mlp":
         return rows
-    if want("swiglu_fwd", "swiglu_bwd", "attn_proj_fwd", "attn_proj_bwd", "attn_core_fwd", "sp_ln_fwd",
-            "sp_ln_bwd"):
+    if want("swiglu_fwd", "swiglu_bwd", "attn_proj_fwd", "attn_proj_bwd", "attn_core_fwd", "attn_core_bwd",
+            "sp_ln_fwd", "sp_ln_bwd"):
         rows += layer_rows(torch, up, bf, I, T, want)
         progress(f"inputs: {rows[-1].config} ready")
     if want("lm_head_fwd", "vocab_ce", "vocab_embed", "vocab_ce_bwd", "lm_head_ce_fused"):
@@ -258,8 +258,19 @@ def layer_rows(torch, up, bf, I, T, want):
     Oc = bf((s4, dq))
     lsec = torch.empty((nqc, s4), dtype=torch.float32, device=dev)
     del ac
+    causal = s4 * (s4 + 1) / 2.0
     rows.append(Row("attn_core_fwd", c4, lambda: T.tp_attn_core_fwd(BF, s4, nqc, nkvc, 128, Qc, Kc, Vc, Oc, lsec),
-                    flops=2.0 * 2.0 * (s4 * (s4 + 1) / 2.0) * 128 * nqc))
+                    flops=2.0 * 2.0 * causal * 128 * nqc))
+    # its backward on the forward's O and lse: five products over the visible half
+    # (the recomputed scores, dP, dV, dK, dQ; the dQ pass's second recompute of the
+    # scores and dP is not counted)
+    dOc = up(I.normal_bf16((s4, nqc * 128), 1.0, 4, I.T_ADO, 0))
+    dQc, dKc, dVc = bf((s4, nqc * 128)), bf((s4, nkvc * 128)), bf((s4, nkvc * 128))
+    nbc = T.tp_attn_core_bwd_workspace(BF, s4, nqc, nkvc, 128)
+    wsc = torch.empty(max(nbc, 256), dtype=torch.uint8, device=dev)
+    rows.append(Row("attn_core_bwd", c4, lambda: T.tp_attn_core_bwd(BF, s4, nqc, nkvc, 128, Qc, Kc, Vc, Oc, dOc, lsec,
+                                                                    dQc, dKc, dVc, wsc, nbc),
+                    flops=5.0 * 2.0 * causal * 128 * nqc))
     # sequence-parallel region on this shard's s/t = 1024 positions: residual + dropout + LayerNorm
     sp = I.sp_inputs(4)
     n_sp, p_sp = sp["n"], sp["p"]
@@ -594,7 +605,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": 1 << 30, "launches": 3}))
         return
-    first = "lm_head_fwd" if args.only in ("vocab_ce", "vocab_ce_bwd") else args.only
+    first = "lm_head_fwd" if args.only in ("vocab_ce", "vocab_ce_bwd") else \
+        "attn_core_fwd" if args.only == "attn_core_bwd" else args.only
     rows = build_rows(torch, args.rows, first)
     progress(f"inputs resident, {len(rows)} rows")
     if args.only:
@@ -606,6 +618,8 @@ def main():
             next(r for r in rows if r.name == "lm_head_fwd").fn()
             if args.only == "vocab_ce_bwd":
                 next(r for r in rows if r.name == "vocab_ce").fn()
+        if args.only == "attn_core_bwd":  # inputs: the forward's O and lse, computed once
+            next(r for r in rows if r.name == "attn_core_fwd").fn()
         rows = keep
     torch.cuda.synchronize()
     for _ in range(args.warmup):

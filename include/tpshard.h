@@ -176,6 +176,50 @@ int tp_attn_core_fwd(int dt, int64_t s, int64_t nq, int64_t nkv, int64_t d,
                      const void *Q, const void *K, const void *V, void *O, float *lse,
                      void *stream);
 
+/* The two halves of tp_attn_proj_bwd as calls of their own, for a layer
+ * backward that runs the attention core's backward between them (the core
+ * needs dO, and produces the dQ, dK, dV the Q/K/V half consumes):
+ *   tp_attn_out_bwd:  dO = dY . Wo^T [s,dq];  dWo = O^T . dY [dq,h]
+ *   tp_attn_qkv_bwd:  dX(i) = dQ.Wq^T + dK.Wk^T + dV.Wv^T [s,h] (f's input);
+ *                     dWq = X^T.dQ, dWk = X^T.dK, dWv = X^T.dV
+ * Same results as the matching outputs of tp_attn_proj_bwd (same kernels and
+ * plans).  ws: device scratch of the size query's bytes (0 possible: then ws
+ * may be NULL), 256-byte aligned, contents garbage on return. */
+size_t tp_attn_out_bwd_workspace(int dt, int64_t s, int64_t h, int64_t dq);
+int tp_attn_out_bwd(int dt, int64_t s, int64_t h, int64_t dq, const void *O, const void *Wo, const void *dY,
+                    void *dO, void *dWo, void *ws, size_t ws_bytes, void *stream);
+size_t tp_attn_qkv_bwd_workspace(int dt, int64_t s, int64_t h, int64_t dq, int64_t dkv);
+int tp_attn_qkv_bwd(int dt, int64_t s, int64_t h, int64_t dq, int64_t dkv,
+                    const void *X, const void *Wq, const void *Wk, const void *Wv,
+                    const void *dQ, const void *dK, const void *dV,
+                    void *dX, void *dWq, void *dWk, void *dWv, void *ws, size_t ws_bytes, void *stream);
+
+/* Backward of tp_attn_core_fwd (the same causal attention of the shard's nq
+ * query heads on its nkv key/value heads).  With P the attention weights of
+ * query head j (KV head g = j / (nq / nkv)), recomputed from Q, K and the
+ * forward's lse instead of stored (the CS336 lecture-8 book, activation-memory
+ * section: FlashAttention recomputes the s x s scores in the backward pass):
+ *     dP = dO_j V_g^T,  D = rowsum(dO_j * O_j),  dS = P * (dP - D)
+ *     dQ_j = dS K_g / sqrt(d)
+ *     dK_g = sum over the query heads j of group g of dS^T Q_j / sqrt(d)
+ *     dV_g = sum over the query heads j of group g of P^T dO_j
+ * a shared KV head's gradient summed over its query heads in increasing head
+ * order ([book] §7.3.4: a card's 8 query heads share its 1 KV head).
+ * Q, O, dO, dQ [s][nq*d]; K, V, dK, dV [s][nkv*d]; lse [nq][s] fp32 from the
+ * forward for the same Q, K, V; O the forward's output.  dt must be
+ * TP_DT_BF16 and d = 128 (TP_EUNSUPPORTED otherwise); nq must be a positive
+ * multiple of nkv, or both 0 (TP_ESHAPE).  P and dS are rounded to bf16
+ * before the products that consume them; all sums are fp32 in a fixed order,
+ * so results are identical run to run.  ws: device scratch of
+ * tp_attn_core_bwd_workspace() bytes, 256-byte aligned, contents garbage on
+ * return (per-query base-2 lse and D, and per-query-head fp32 partial dK and
+ * dV: about 8 * nq * s * d bytes). */
+size_t tp_attn_core_bwd_workspace(int dt, int64_t s, int64_t nq, int64_t nkv, int64_t d);
+int tp_attn_core_bwd(int dt, int64_t s, int64_t nq, int64_t nkv, int64_t d,
+                     const void *Q, const void *K, const void *V, const void *O, const void *dO,
+                     const float *lse, void *dQ, void *dK, void *dV,
+                     void *ws, size_t ws_bytes, void *stream);
+
 /* ------------------------------------------------------------------------ */
 /* Sequence-parallel region ([book] §7.3.6)                                   */
 /* ------------------------------------------------------------------------ */

@@ -79,6 +79,13 @@ hipError_t tp_launch_vocab_embed(int elem_bytes, int64_t n, int64_t Vs, int64_t 
 hipError_t tp_launch_attn_fwd(int64_t s, int64_t nq, int64_t nkv, const void *Q, const void *K, const void *V,
                               void *O, float *lse, hipStream_t st);
 
+// backward of the attention core: D = rowsum(dO * O) and dQ, then per-query-head
+// partial dK / dV, then their fixed-order sum over each KV head's query heads
+size_t tp_attn_bwd_ws_bytes(int64_t s, int64_t nq);
+hipError_t tp_launch_attn_bwd(int64_t s, int64_t nq, int64_t nkv, const void *Q, const void *K, const void *V,
+                              const void *O, const void *dO, const float *lse, void *dQ, void *dK, void *dV,
+                              void *ws, hipStream_t st);
+
 // sequence-parallel region (residual + dropout + LayerNorm) on [n, h] bf16 rows
 int tp_sp_ln_passes(int64_t h);        // register passes per row (h <= 8192: 1)
 int tp_sp_ln_bwd_grid(int64_t n, int64_t h);  // partial sums of dgamma/dbeta the backward writes

@@ -1026,6 +1026,88 @@ int tp_attn_proj_bwd(int dt, int64_t s, int64_t h, int64_t dq, int64_t dkv, cons
   return ok();
 }
 
+// The two halves of tp_attn_proj_bwd as calls of their own, for a layer
+// backward that runs the attention core's backward between them: the output
+// projection's (dO, dWo) first, then the Q/K/V projections' (dX, dWq/k/v).
+size_t tp_attn_out_bwd_workspace(int dt, int64_t s, int64_t h, int64_t dq) {
+  Checker c;
+  c.dtype(dt, true, "tp_attn_out_bwd_workspace");
+  c.dim(s, "s") && c.dim(h, "h") && c.dim(dq, "dq");
+  if (c.status) return 0;
+  const AttnBwdLayout L = attn_bwd_layout(dt, s, h, dq, 0);
+  return L.part2_bytes;
+}
+
+int tp_attn_out_bwd(int dt, int64_t s, int64_t h, int64_t dq, const void *O, const void *Wo, const void *dY,
+                    void *dO, void *dWo, void *ws, size_t ws_bytes, void *stream) {
+  Checker c;
+  int64_t nx, nwq, nq;
+  c.dtype(dt, true, "tp_attn_out_bwd");
+  c.dim(s, "s") && c.dim(h, "h") && c.dim(dq, "dq");
+  c.elems(s, h, nx, "dY") && c.elems(h, dq, nwq, "Wo") && c.elems(s, dq, nq, "O");
+  c.ptr(O, nq, "O") && c.ptr(Wo, nwq, "Wo") && c.ptr(dY, nx, "dY") && c.ptr(dO, nq, "dO") && c.ptr(dWo, nwq, "dWo");
+  if (c.status) return c.status;
+  const AttnBwdLayout L = attn_bwd_layout(dt, s, h, dq, 0);
+  ws_ok(c, ws, ws_bytes, L.part2_bytes, "tp_attn_out_bwd");
+  if (c.status) return c.status;
+  Ptrs pw;
+  pw.A[0] = O; pw.lda[0] = dq;
+  pw.B[0] = dY; pw.ldb[0] = h;
+  pw.C[0] = dWo; pw.ldc[0] = h;
+  Ptrs po;
+  po.A[0] = dY; po.lda[0] = h;
+  po.B[0] = Wo; po.ldb[0] = h;
+  po.C[0] = dO; po.ldc[0] = dq;
+  pw.stream_out = po.stream_out = 1;
+  if (int e = run_pair(L.g_dwo, pw, L.g_do, po, dt, ws, (hipStream_t)stream, "tp_attn_out_bwd dWo GEMM",
+                       "tp_attn_out_bwd dO GEMM"))
+    return e;
+  return ok();
+}
+
+size_t tp_attn_qkv_bwd_workspace(int dt, int64_t s, int64_t h, int64_t dq, int64_t dkv) {
+  Checker c;
+  c.dtype(dt, true, "tp_attn_qkv_bwd_workspace");
+  c.dim(s, "s") && c.dim(h, "h") && c.dim(dq, "dq") && c.dim(dkv, "dkv");
+  if (c.status) return 0;
+  return attn_bwd_layout(dt, s, h, dq, dkv).part1_bytes;
+}
+
+int tp_attn_qkv_bwd(int dt, int64_t s, int64_t h, int64_t dq, int64_t dkv, const void *X, const void *Wq,
+                    const void *Wk, const void *Wv, const void *dQ, const void *dK, const void *dV, void *dX,
+                    void *dWq, void *dWk, void *dWv, void *ws, size_t ws_bytes, void *stream) {
+  Checker c;
+  int64_t nx, nwq, nwk, nq, nk;
+  c.dtype(dt, true, "tp_attn_qkv_bwd");
+  c.dim(s, "s") && c.dim(h, "h") && c.dim(dq, "dq") && c.dim(dkv, "dkv");
+  c.elems(s, h, nx, "X") && c.elems(h, dq, nwq, "Wq") && c.elems(h, dkv, nwk, "Wk") &&
+      c.elems(s, dq, nq, "dQ") && c.elems(s, dkv, nk, "dK");
+  c.ptr(X, nx, "X") && c.ptr(Wq, nwq, "Wq") && c.ptr(Wk, nwk, "Wk") && c.ptr(Wv, nwk, "Wv") &&
+      c.ptr(dQ, nq, "dQ") && c.ptr(dK, nk, "dK") && c.ptr(dV, nk, "dV") && c.ptr(dX, nx, "dX") &&
+      c.ptr(dWq, nwq, "dWq") && c.ptr(dWk, nwk, "dWk") && c.ptr(dWv, nwk, "dWv");
+  if (c.status) return c.status;
+  const AttnBwdLayout L = attn_bwd_layout(dt, s, h, dq, dkv);
+  ws_ok(c, ws, ws_bytes, L.part1_bytes, "tp_attn_qkv_bwd");
+  if (c.status) return c.status;
+  Ptrs pw;
+  pw.A[0] = X; pw.lda[0] = h;
+  pw.B[0] = dQ; pw.B[1] = dK; pw.B[2] = dV;
+  pw.ldb[0] = dq; pw.ldb[1] = pw.ldb[2] = dkv;
+  pw.C[0] = dWq; pw.C[1] = dWk; pw.C[2] = dWv;
+  pw.ldc[0] = dq; pw.ldc[1] = pw.ldc[2] = dkv;
+  Ptrs px;
+  px.A[0] = dQ; px.A[1] = dK; px.A[2] = dV;
+  px.lda[0] = dq; px.lda[1] = px.lda[2] = dkv;
+  px.B[0] = Wq; px.B[1] = Wk; px.B[2] = Wv;
+  px.ldb[0] = dq; px.ldb[1] = px.ldb[2] = dkv;
+  px.C[0] = dX; px.ldc[0] = h;
+  pw.stream_out = px.stream_out = 1;
+  if (int e = run_pair(L.g_dwqkv, pw, L.g_dx, px, dt, ws, (hipStream_t)stream, "tp_attn_qkv_bwd dWqkv GEMM",
+                       "tp_attn_qkv_bwd dX GEMM"))
+    return e;
+  return ok();
+}
+
 // ------------------------------------------------------------------ vocab
 int tp_lm_head_fwd(int dt, int64_t s, int64_t h, int64_t Vs, const void *Hf, const void *Wlm, float *logits,
                    void *stream) {
@@ -1095,6 +1177,37 @@ int tp_attn_core_fwd(int dt, int64_t s, int64_t nq, int64_t nkv, int64_t d, cons
   if (c.status) return c.status;
   hipError_t e = tp_launch_attn_fwd(s, nq, nkv, Q, K, V, O, lse, (hipStream_t)stream);
   if (e != hipSuccess) return fail(TP_EHIP, "tp_attn_core_fwd: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t tp_attn_core_bwd_workspace(int dt, int64_t s, int64_t nq, int64_t nkv, int64_t d) {
+  Checker c;
+  c.dtype(dt, false, "tp_attn_core_bwd_workspace");
+  c.dim(s, "s") && c.dim(nq, "nq") && c.dim(nkv, "nkv") && c.dim(d, "d");
+  if (!c.status && d != 128) return 0;
+  if (c.status) return 0;
+  return tp_attn_bwd_ws_bytes(s, nq);
+}
+
+int tp_attn_core_bwd(int dt, int64_t s, int64_t nq, int64_t nkv, int64_t d, const void *Q, const void *K,
+                     const void *V, const void *O, const void *dO, const float *lse, void *dQ, void *dK, void *dV,
+                     void *ws, size_t ws_bytes, void *stream) {
+  Checker c;
+  int64_t nqe, nke, nl;
+  c.dtype(dt, false, "tp_attn_core_bwd");
+  c.dim(s, "s") && c.dim(nq, "nq") && c.dim(nkv, "nkv") && c.dim(d, "d");
+  if (!c.status && d != 128) c.status = fail(TP_EUNSUPPORTED, "tp_attn_core_bwd: head dim %lld (only 128)", (long long)d);
+  if (!c.status && (nq % (nkv ? nkv : 1) != 0 || (nkv == 0) != (nq == 0)))
+    c.status = fail(TP_ESHAPE, "tp_attn_core_bwd: nq = %lld is not a positive multiple of nkv = %lld "
+                    "(or both 0)", (long long)nq, (long long)nkv);
+  c.elems(s, nq * d, nqe, "Q") && c.elems(s, nkv * d, nke, "K") && c.elems(nq, s, nl, "lse");
+  c.ptr(Q, nqe, "Q") && c.ptr(K, nke, "K") && c.ptr(V, nke, "V") && c.ptr(O, nqe, "O") && c.ptr(dO, nqe, "dO") &&
+      c.ptr(lse, nl, "lse") && c.ptr(dQ, nqe, "dQ") && c.ptr(dK, nke, "dK") && c.ptr(dV, nke, "dV");
+  if (c.status) return c.status;
+  ws_ok(c, ws, ws_bytes, nqe > 0 ? tp_attn_bwd_ws_bytes(s, nq) : 0, "tp_attn_core_bwd");
+  if (c.status) return c.status;
+  hipError_t e = tp_launch_attn_bwd(s, nq, nkv, Q, K, V, O, dO, lse, dQ, dK, dV, ws, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(TP_EHIP, "tp_attn_core_bwd: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -28,6 +28,7 @@ T_X, T_W1, T_W2, T_DY, T_WG, T_WU, T_WD, T_WQ, T_WK, T_WV, T_WO, T_O, T_DQ, T_DK
     T_DV, T_HF, T_WLM, T_TGT, T_TABLE, T_IDS, T_LOGITS = range(21)
 T_AQ, T_AK, T_AV = 21, 22, 23   # attention-core inputs
 T_SPY, T_SPX, T_SPMASK, T_SPG, T_SPB, T_SPDZ, T_SPDUN = range(24, 31)   # sequence-parallel region
+T_ADO = 31   # gradient arriving at the attention core's output
 
 
 def _rng(config: int, tensor: int, shard: int = 0) -> np.random.Generator:

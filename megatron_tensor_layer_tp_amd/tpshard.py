@@ -38,6 +38,12 @@ _SIGS = {
     "tp_vocab_ce": (_int, [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
     "tp_vocab_ce_bwd": (_int, [_int, _i64, _i64, _i64] + [_vp] * 6 + [_vp]),
     "tp_attn_core_fwd": (_int, [_int, _i64, _i64, _i64, _i64] + [_vp] * 5 + [_vp]),
+    "tp_attn_core_bwd_workspace": (_sz, [_int, _i64, _i64, _i64, _i64]),
+    "tp_attn_core_bwd": (_int, [_int, _i64, _i64, _i64, _i64] + [_vp] * 9 + [_vp, _sz, _vp]),
+    "tp_attn_out_bwd_workspace": (_sz, [_int, _i64, _i64, _i64]),
+    "tp_attn_out_bwd": (_int, [_int, _i64, _i64, _i64] + [_vp] * 5 + [_vp, _sz, _vp]),
+    "tp_attn_qkv_bwd_workspace": (_sz, [_int, _i64, _i64, _i64, _i64]),
+    "tp_attn_qkv_bwd": (_int, [_int, _i64, _i64, _i64, _i64] + [_vp] * 11 + [_vp, _sz, _vp]),
     "tp_sp_ln_fwd": (_int, [_int, _i64, _i64, ctypes.c_float, ctypes.c_float] + [_vp] * 9 + [_vp]),
     "tp_sp_ln_bwd_workspace": (_sz, [_int, _i64, _i64]),
     "tp_sp_ln_bwd": (_int, [_int, _i64, _i64, ctypes.c_float] + [_vp] * 11 + [_vp, _sz, _vp]),
@@ -164,6 +170,24 @@ def tp_attn_proj_bwd(dt, s, h, dq, dkv, X, Wq, Wk, Wv, O, Wo, dQ, dK, dV, dY, dX
                  _ptr(dWk), _ptr(dWv), _ptr(dO), _ptr(dWo), _ptr(ws), ws_bytes, _stream(stream))
 
 
+def tp_attn_out_bwd_workspace(dt, s, h, dq) -> int:
+    return lib().tp_attn_out_bwd_workspace(dt, s, h, dq)
+
+
+def tp_attn_out_bwd(dt, s, h, dq, O, Wo, dY, dO, dWo, ws, ws_bytes, stream=None):
+    return _call("tp_attn_out_bwd", dt, s, h, dq, _ptr(O), _ptr(Wo), _ptr(dY), _ptr(dO), _ptr(dWo), _ptr(ws),
+                 ws_bytes, _stream(stream))
+
+
+def tp_attn_qkv_bwd_workspace(dt, s, h, dq, dkv) -> int:
+    return lib().tp_attn_qkv_bwd_workspace(dt, s, h, dq, dkv)
+
+
+def tp_attn_qkv_bwd(dt, s, h, dq, dkv, X, Wq, Wk, Wv, dQ, dK, dV, dX, dWq, dWk, dWv, ws, ws_bytes, stream=None):
+    return _call("tp_attn_qkv_bwd", dt, s, h, dq, dkv, _ptr(X), _ptr(Wq), _ptr(Wk), _ptr(Wv), _ptr(dQ), _ptr(dK),
+                 _ptr(dV), _ptr(dX), _ptr(dWq), _ptr(dWk), _ptr(dWv), _ptr(ws), ws_bytes, _stream(stream))
+
+
 # ---------------------------------------------------------------- vocab
 def tp_lm_head_fwd(dt, s, h, Vs, Hf, Wlm, logits, stream=None):
     return _call("tp_lm_head_fwd", dt, s, h, Vs, _ptr(Hf), _ptr(Wlm), _ptr(logits), _stream(stream))
@@ -172,6 +196,15 @@ def tp_lm_head_fwd(dt, s, h, Vs, Hf, Wlm, logits, stream=None):
 def tp_attn_core_fwd(dt, s, nq, nkv, d, Q, K, V, O, lse, stream=None):
     return _call("tp_attn_core_fwd", dt, s, nq, nkv, d, _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(lse),
                  _stream(stream))
+
+
+def tp_attn_core_bwd_workspace(dt, s, nq, nkv, d) -> int:
+    return lib().tp_attn_core_bwd_workspace(dt, s, nq, nkv, d)
+
+
+def tp_attn_core_bwd(dt, s, nq, nkv, d, Q, K, V, O, dO, lse, dQ, dK, dV, ws, ws_bytes, stream=None):
+    return _call("tp_attn_core_bwd", dt, s, nq, nkv, d, _ptr(Q), _ptr(K), _ptr(V), _ptr(O), _ptr(dO), _ptr(lse),
+                 _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(ws), ws_bytes, _stream(stream))
 
 
 def tp_sp_ln_fwd(dt, n, h, p, eps, y, x, mask, gamma, beta, u, z, mean, rstd, stream=None):

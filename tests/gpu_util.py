@@ -79,7 +79,8 @@ BF16_REL = 2.0 ** -7
 BF16_RMS = 2.0 ** -5
 
 
-def elem_bound(got: np.ndarray, want: np.ndarray, name: str, rel: float = BF16_REL, rms_frac: float = BF16_RMS):
+def elem_bound(got: np.ndarray, want: np.ndarray, name: str, rel: float = BF16_REL, rms_frac: float = BF16_RMS,
+               atol: float = 0.0):
     got = np.asarray(got, dtype=np.float64)
     want = np.asarray(want, dtype=np.float64)
     assert got.shape == want.shape, (name, got.shape, want.shape)
@@ -88,7 +89,7 @@ def elem_bound(got: np.ndarray, want: np.ndarray, name: str, rel: float = BF16_R
     assert np.all(np.isfinite(got)), f"{name}: non-finite values in the GPU result"
     rms = float(np.sqrt(np.mean(want * want)))
     err = np.abs(got - want)
-    lim = rel * np.abs(want) + rms_frac * rms
+    lim = rel * np.abs(want) + rms_frac * rms + atol
     bad = np.argwhere(err > lim)
     assert bad.size == 0, (f"{name}: {bad.shape[0]} of {want.size} entries outside |err| <= {rel:.3g}|want| + "
                            f"{rms_frac:.3g} rms; first at {tuple(bad[0])}: got {got[tuple(bad[0])]!r}, "
@@ -96,10 +97,11 @@ def elem_bound(got: np.ndarray, want: np.ndarray, name: str, rel: float = BF16_R
 
 
 def check_bf16(got: np.ndarray, want: np.ndarray, name: str, tol: float = 5e-3, rel: float = BF16_REL,
-               rms_frac: float = BF16_RMS) -> float:
+               rms_frac: float = BF16_RMS, atol: float = 0.0) -> float:
     """The parity bar for a bf16 output (or a sample of one): relative
-    Frobenius error <= tol over the whole tensor and the element-wise bound."""
+    Frobenius error <= tol over the whole tensor and the element-wise bound
+    (``atol``: an absolute floor for outputs that are exactly zero)."""
     err = rel_fro(got, want)
     assert err <= tol, f"{name}: relative Frobenius error {err:.3e} > {tol}"
-    elem_bound(got, want, name, rel, rms_frac)
+    elem_bound(got, want, name, rel, rms_frac, atol)
     return err

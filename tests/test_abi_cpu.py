@@ -34,7 +34,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert len(names) == 22, names
+    assert len(names) == 28, names
     raw = ctypes.CDLL(T.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -206,3 +206,57 @@ def test_sp_validation(L):
     assert _st(L, "tp_sp_ln_bwd", *b, A16 + 64, need, None) == T.TP_EALIGN
     assert _st(L, "tp_sp_ln_fwd", T.TP_DT_BF16, 0, 64, C.c_float(0.1), C.c_float(1e-5), None, None, None, A16, A16,
                None, None, None, None, None) == T.TP_OK
+
+
+def test_attn_core_bwd_validation(L):
+    need = T.tp_attn_core_bwd_workspace(T.TP_DT_BF16, 8192, 8, 1, 128)
+    # per-query-head fp32 partials of dK and dV, plus the per-query statistics
+    assert need >= 2 * 8 * 8192 * 128 * 4 + 8 * 8192 * 2 * 4
+    assert need == T.tp_attn_core_bwd_workspace(T.TP_DT_BF16, 8192, 8, 1, 128)
+    assert T.tp_attn_core_bwd_workspace(T.TP_DT_BF16, 8192, 8, 1, 64) == 0
+    args = [T.TP_DT_BF16, 8192, 8, 1, 128] + [A16] * 9
+    assert _st(L, "tp_attn_core_bwd", *args, A16, need - 1, None) == T.TP_EWORKSPACE
+    assert _st(L, "tp_attn_core_bwd", *args, A16 + 32, need, None) == T.TP_EALIGN
+    bad = list(args)
+    bad[4] = 64
+    assert _st(L, "tp_attn_core_bwd", *bad, A16, need, None) == T.TP_EUNSUPPORTED
+    bad = list(args)
+    bad[0] = T.TP_DT_F32
+    assert _st(L, "tp_attn_core_bwd", *bad, A16, need, None) == T.TP_EUNSUPPORTED
+    bad = list(args)
+    bad[3] = 3
+    assert _st(L, "tp_attn_core_bwd", *bad, A16, need, None) == T.TP_ESHAPE
+    bad = list(args)
+    bad[2], bad[3] = 0, 1  # no query heads for a KV head
+    assert _st(L, "tp_attn_core_bwd", *bad, A16, need, None) == T.TP_ESHAPE
+    bad = list(args)
+    bad[10] = None  # lse
+    assert _st(L, "tp_attn_core_bwd", *bad, A16, need, None) == T.TP_EINVAL
+    assert "lse" in T.tp_last_error()
+    bad = list(args)
+    bad[13] = A16 + 2  # dV
+    assert _st(L, "tp_attn_core_bwd", *bad, A16, need, None) == T.TP_EALIGN
+    # nothing to compute: no positions
+    assert _st(L, "tp_attn_core_bwd", T.TP_DT_BF16, 0, 8, 1, 128, *([None] * 9), None, 0, None) == T.TP_OK
+
+
+def test_attn_proj_bwd_halves_validation(L):
+    no = T.tp_attn_out_bwd_workspace(T.TP_DT_BF16, 8192, 8192, 1024)
+    nq = T.tp_attn_qkv_bwd_workspace(T.TP_DT_BF16, 8192, 8192, 1024, 128)
+    # the halves' workspaces are the whole call's two regions
+    assert no + nq == T.tp_attn_proj_bwd_workspace(T.TP_DT_BF16, 8192, 8192, 1024, 128)
+    o = [T.TP_DT_BF16, 8192, 8192, 1024] + [A16] * 5
+    if no:
+        assert _st(L, "tp_attn_out_bwd", *o, A16, no - 1, None) == T.TP_EWORKSPACE
+    bad = list(o)
+    bad[6] = None  # dY
+    assert _st(L, "tp_attn_out_bwd", *bad, A16, no, None) == T.TP_EINVAL
+    q = [T.TP_DT_BF16, 8192, 8192, 1024, 128] + [A16] * 11
+    if nq:
+        assert _st(L, "tp_attn_qkv_bwd", *q, A16, nq - 1, None) == T.TP_EWORKSPACE
+    bad = list(q)
+    bad[4] = -1
+    assert _st(L, "tp_attn_qkv_bwd", *bad, A16, nq, None) == T.TP_ESHAPE
+    bad = list(q)
+    bad[11] = A16 + 8  # dX
+    assert _st(L, "tp_attn_qkv_bwd", *bad, A16, nq, None) == T.TP_EALIGN
