@@ -316,6 +316,23 @@ int tp_lm_head_ce_fwd(int dt, int64_t s, int64_t h, int64_t Vs, int64_t vocab_st
                       float *lmax, float *lsumexp, float *tlogit,
                       void *ws, size_t ws_bytes, void *stream);
 
+/* The same as tp_lm_head_ce_fwd without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  The per-part statistics go to a
+ * scratch array the library holds on each GPU it runs on, of
+ * tp_lm_head_ce_noalloc_max_bytes() = 32 MiB (enough for s * Vs up to about
+ * 2.8e6 * 256 / 12, e.g. s = 8192 positions of a 16032-wide vocab shard):
+ * larger requests return TP_EWORKSPACE before anything is enqueued.  The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ * The stream must belong to the current device.  Every call on one GPU shares
+ * that GPU's scratch: calls that overlap on one GPU (concurrent streams,
+ * several host threads) race and must be serialised by the caller.  Nothing
+ * in the scratch needs to start at zero: each call writes every slot it reads. */
+size_t tp_lm_head_ce_noalloc_max_bytes(void);
+int tp_lm_head_ce_fwd_noalloc(int dt, int64_t s, int64_t h, int64_t Vs, int64_t vocab_start,
+                              const void *Hf, const void *Wlm, const int64_t *target,
+                              float *lmax, float *lsumexp, float *tlogit, void *stream);
+
 /* Embedding rows of a vocab shard: out[r,:] = table[ids[r]-vocab_start, :]
  * when vocab_start <= ids[r] < vocab_start+Vs, else the zero vector (all bits
  * 0).  table [Vs,h], out [n,h]; dt is the element type (rows are copied bit

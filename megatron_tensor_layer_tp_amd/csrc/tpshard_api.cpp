@@ -17,6 +17,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <vector>
 #include <string>
 
@@ -101,6 +102,17 @@ struct Checker {
     return true;
   }
 };
+
+// Scratch of the allocation-free fused LM head + CE call
+// (tp_lm_head_ce_fwd_noalloc): a file-scope device array, 32 MiB, of which each
+// GPU the library runs on holds its own copy until the process ends.  In host
+// code `scratch` names a host-side stand-in, not the device array: kernels get
+// the per-device address hipGetSymbolAddress returns, fetched once per device
+// with that device current (scratch_ptr below).
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+}  // namespace
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+namespace {
 
 // ---------------------------------------------------------------- planning
 struct Plan {
@@ -1270,22 +1282,29 @@ size_t tp_lm_head_ce_workspace(int dt, int64_t s, int64_t h, int64_t Vs) {
   return lm_ce_plan(s, h, Vs).bytes;
 }
 
-int tp_lm_head_ce_fwd(int dt, int64_t s, int64_t h, int64_t Vs, int64_t vocab_start, const void *Hf,
-                      const void *Wlm, const int64_t *target, float *lmax, float *lsumexp, float *tlogit,
-                      void *ws, size_t ws_bytes, void *stream) {
-  Checker c;
+}  // extern "C"
+
+namespace {
+
+// Argument checks shared by the fused LM head + CE calls.
+int lm_ce_check(Checker &c, const char *call, int dt, int64_t s, int64_t h, int64_t Vs, int64_t vocab_start,
+                const void *Hf, const void *Wlm, const int64_t *target, float *lmax, float *lsumexp, float *tlogit) {
   int64_t nh, nw;
-  c.dtype(dt, false, "tp_lm_head_ce_fwd");
+  c.dtype(dt, false, call);
   c.dim(s, "s") && c.dim(h, "h") && c.dim(Vs, "Vs");
   if (!c.status && vocab_start < 0) c.status = fail(TP_ESHAPE, "vocab_start = %lld < 0", (long long)vocab_start);
   c.elems(s, h, nh, "Hf") && c.elems(h, Vs, nw, "Wlm");
   c.ptr(Hf, nh, "Hf") && c.ptr(Wlm, nw, "Wlm") && c.ptr(target, s, "target") && c.ptr(lmax, s, "lmax") &&
       c.ptr(lsumexp, s, "lsumexp") && c.ptr(tlogit, s, "tlogit");
-  if (c.status) return c.status;
-  const LmCePlan L = lm_ce_plan(s, h, Vs);
-  ws_ok(c, ws, ws_bytes, L.bytes, "tp_lm_head_ce_fwd");
-  if (c.status) return c.status;
-  hipStream_t st = (hipStream_t)stream;
+  return c.status;
+}
+
+// The GEMM with the CE-statistics epilogue, then the merge of the parts; ws
+// holds the plan's partial statistics (every slot the merge reads is written
+// by the GEMM of the same call, so ws needs no clearing).
+int lm_ce_launch(const LmCePlan &L, int64_t s, int64_t h, int64_t Vs, int64_t vocab_start, const void *Hf,
+                 const void *Wlm, const int64_t *target, float *lmax, float *lsumexp, float *tlogit, void *ws,
+                 hipStream_t st, const char *call) {
   Ptrs q;
   q.A[0] = Hf; q.lda[0] = h;
   q.B[0] = Wlm; q.ldb[0] = Vs;
@@ -1296,8 +1315,68 @@ int tp_lm_head_ce_fwd(int dt, int64_t s, int64_t h, int64_t Vs, int64_t vocab_st
   if (e == hipSuccess)
     e = tp_launch_ce_merge((const float *)ws, L.parts, L.width, s, Vs, vocab_start, target, lmax, lsumexp, tlogit,
                            st);
-  if (e != hipSuccess) return fail(TP_EHIP, "tp_lm_head_ce_fwd: %s", hipGetErrorString(e));
+  if (e != hipSuccess) return fail(TP_EHIP, "%s: %s", call, hipGetErrorString(e));
   return ok();
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// the current device's address of `scratch`, or an error status
+int scratch_ptr(void **out, const char *call) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(TP_EHIP, "%s: hipGetDevice: %s", call, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(TP_EUNSUPPORTED, "%s: device %d beyond %d", call, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(TP_EHIP, "%s: hipGetSymbolAddress(scratch) on device %d: %s", call, dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tp_lm_head_ce_fwd(int dt, int64_t s, int64_t h, int64_t Vs, int64_t vocab_start, const void *Hf,
+                      const void *Wlm, const int64_t *target, float *lmax, float *lsumexp, float *tlogit,
+                      void *ws, size_t ws_bytes, void *stream) {
+  Checker c;
+  if (lm_ce_check(c, "tp_lm_head_ce_fwd", dt, s, h, Vs, vocab_start, Hf, Wlm, target, lmax, lsumexp, tlogit))
+    return c.status;
+  const LmCePlan L = lm_ce_plan(s, h, Vs);
+  ws_ok(c, ws, ws_bytes, L.bytes, "tp_lm_head_ce_fwd");
+  if (c.status) return c.status;
+  return lm_ce_launch(L, s, h, Vs, vocab_start, Hf, Wlm, target, lmax, lsumexp, tlogit, ws, (hipStream_t)stream,
+                      "tp_lm_head_ce_fwd");
+}
+
+size_t tp_lm_head_ce_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+int tp_lm_head_ce_fwd_noalloc(int dt, int64_t s, int64_t h, int64_t Vs, int64_t vocab_start, const void *Hf,
+                              const void *Wlm, const int64_t *target, float *lmax, float *lsumexp, float *tlogit,
+                              void *stream) {
+  Checker c;
+  if (lm_ce_check(c, "tp_lm_head_ce_fwd_noalloc", dt, s, h, Vs, vocab_start, Hf, Wlm, target, lmax, lsumexp,
+                  tlogit))
+    return c.status;
+  const LmCePlan L = lm_ce_plan(s, h, Vs);
+  if (L.bytes > kNoAllocScratchBytes)
+    return fail(TP_EWORKSPACE, "tp_lm_head_ce_fwd_noalloc: s = %lld, Vs = %lld need %zu bytes of scratch; the "
+                "allocation-free call holds %zu (use tp_lm_head_ce_fwd with a workspace)", (long long)s,
+                (long long)Vs, L.bytes, kNoAllocScratchBytes);
+  if (s == 0) return ok();
+  void *ws = nullptr;
+  if (int e = scratch_ptr(&ws, "tp_lm_head_ce_fwd_noalloc")) return e;
+  return lm_ce_launch(L, s, h, Vs, vocab_start, Hf, Wlm, target, lmax, lsumexp, tlogit, ws, (hipStream_t)stream,
+                      "tp_lm_head_ce_fwd_noalloc");
 }
 
 int tp_vocab_embed(int dt, int64_t n, int64_t Vs, int64_t h, int64_t vocab_start, const int64_t *ids,

@@ -49,6 +49,8 @@ _SIGS = {
     "tp_sp_ln_bwd": (_int, [_int, _i64, _i64, ctypes.c_float] + [_vp] * 11 + [_vp, _sz, _vp]),
     "tp_lm_head_ce_workspace": (_sz, [_int, _i64, _i64, _i64]),
     "tp_lm_head_ce_fwd": (_int, [_int, _i64, _i64, _i64, _i64] + [_vp] * 6 + [_vp, _sz, _vp]),
+    "tp_lm_head_ce_noalloc_max_bytes": (_sz, []),
+    "tp_lm_head_ce_fwd_noalloc": (_int, [_int, _i64, _i64, _i64, _i64] + [_vp] * 6 + [_vp]),
     "tp_vocab_embed": (_int, [_int, _i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp]),
     "tp_status_string": (ctypes.c_char_p, [_int]),
     "tp_last_error": (ctypes.c_char_p, []),
@@ -235,6 +237,15 @@ def tp_lm_head_ce_fwd(dt, s, h, Vs, vocab_start, Hf, Wlm, target, lmax, lsumexp,
                       stream=None):
     return _call("tp_lm_head_ce_fwd", dt, s, h, Vs, vocab_start, _ptr(Hf), _ptr(Wlm), _ptr(target), _ptr(lmax),
                  _ptr(lsumexp), _ptr(tlogit), _ptr(ws), ws_bytes, _stream(stream))
+
+
+def tp_lm_head_ce_noalloc_max_bytes() -> int:
+    return lib().tp_lm_head_ce_noalloc_max_bytes()
+
+
+def tp_lm_head_ce_fwd_noalloc(dt, s, h, Vs, vocab_start, Hf, Wlm, target, lmax, lsumexp, tlogit, stream=None):
+    return _call("tp_lm_head_ce_fwd_noalloc", dt, s, h, Vs, vocab_start, _ptr(Hf), _ptr(Wlm), _ptr(target),
+                 _ptr(lmax), _ptr(lsumexp), _ptr(tlogit), _stream(stream))
 
 
 def tp_vocab_ce(s, Vs, vocab_start, logits, target, lmax, lsumexp, tlogit, stream=None):

@@ -34,7 +34,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = header_functions()
-    assert len(names) == 28, names
+    assert len(names) == 30, names
     raw = ctypes.CDLL(T.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
@@ -260,3 +260,24 @@ def test_attn_proj_bwd_halves_validation(L):
     bad = list(q)
     bad[11] = A16 + 8  # dX
     assert _st(L, "tp_attn_qkv_bwd", *bad, A16, nq, None) == T.TP_EALIGN
+
+
+def test_lm_head_ce_noalloc_validation(L):
+    cap = T.tp_lm_head_ce_noalloc_max_bytes()
+    assert cap == 32 << 20
+    args = [T.TP_DT_BF16, 8192, 8192, 16032, 0] + [A16] * 6 + [None]
+    bad = list(args)
+    bad[0] = T.TP_DT_F32
+    assert _st(L, "tp_lm_head_ce_fwd_noalloc", *bad) == T.TP_EUNSUPPORTED
+    bad = list(args)
+    bad[7] = None  # target
+    assert _st(L, "tp_lm_head_ce_fwd_noalloc", *bad) == T.TP_EINVAL
+    # beyond the scratch: refused before anything is enqueued
+    bad = list(args)
+    bad[1] = 16384
+    assert T.tp_lm_head_ce_workspace(T.TP_DT_BF16, 16384, 8192, 16032) > cap
+    assert _st(L, "tp_lm_head_ce_fwd_noalloc", *bad) == T.TP_EWORKSPACE
+    assert "scratch" in T.tp_last_error()
+    # nothing to compute: no positions (no device touched)
+    assert _st(L, "tp_lm_head_ce_fwd_noalloc", T.TP_DT_BF16, 0, 64, 100, 0, None, A16, None, None, None, None,
+               None) == T.TP_OK
