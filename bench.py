@@ -49,8 +49,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a 1 GiB device-to-device copy (HBM counter calibration)")
-    p.add_argument("--traffic-summary", default=None, metavar="DIR",
-                   help="reduce rocprofv3 FETCH_SIZE/WRITE_SIZE passes under DIR to profiles/hbm_traffic.json")
+    p.add_argument("--counter-summary", default=None, metavar="DIR",
+                   help="reduce the rocprofv3 counter passes under DIR (DIR/<row>/<fetch|write|sq>, DIR/copy/"
+                        "<fetch|write>) to profiles/hbm_traffic.json and print a markdown table")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU time of the oracle sample")
     return p.parse_args()
@@ -509,79 +510,175 @@ def cpu_baseline(seconds: float):
     return out
 
 
-def traffic_for(kernel_key: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None when the kernel source changed since the counters were taken."""
+# ---------------------------------------------------------------------------
+# rocprofv3 counter passes -> per-row summaries
+# ---------------------------------------------------------------------------
+ROW_NAMES = ["mlp_fwd_gpt3", "mlp_bwd_gpt3", "mlp_fwd_gpt2", "mlp_bwd_gpt2", "swiglu_fwd", "swiglu_bwd",
+             "attn_proj_fwd", "attn_proj_bwd", "attn_core_fwd", "attn_core_bwd", "sp_ln_fwd", "sp_ln_bwd",
+             "lm_head_fwd", "vocab_ce", "vocab_embed", "vocab_ce_bwd", "lm_head_ce_fused"]
+COUNTER_PASSES = {"fetch": ["FETCH_SIZE"], "write": ["WRITE_SIZE"],
+                  "sq": ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CU_CYCLES", "SQ_INSTS_MFMA"]}
+
+
+def alg_bytes(row: str) -> float:
+    """Compulsory HBM bytes of one call of a bench row: every input read once,
+    every output (and every intermediate a call must hand between its launches)
+    written once -- the per-unit figures times the workload's sizes."""
+    from megatron_tensor_layer_tp_amd import inputs as I
+    b = 2.0
+    if row.startswith("mlp_"):
+        c = I.CONFIGS[3 if row.endswith("gpt3") else 2]
+        s, h, ft = c["s"], c["h"], c["f"] // c["t"]
+        if row.startswith("mlp_fwd"):
+            return b * (s * h + 2 * h * ft + 2 * s * ft + s * h)
+        # X, W1, W2, Z, H, dY read; dX, dW1, dW2 written; dZ written and read back
+        return b * (2 * s * h + 2 * h * ft + 2 * s * ft) + b * (s * h + 2 * h * ft) + 2 * b * s * ft
+    c = I.CONFIGS[4]
+    s, h = c["s"], c["h"]
+    ft = c["f"] // c["t"]
+    dq, dkv = c["dq_full"] // c["t"], c["dkv_full"] // c["t"]
+    nq = dq // 128
+    c5 = I.CONFIGS[5]
+    s5, h5, Vs = c5["s"], c5["h"], c5["V"] // c5["t"]
+    n_sp = s // c["t"]
+    table = {
+        "swiglu_fwd": b * (s * h + 3 * h * ft + 3 * s * ft + s * h),
+        "swiglu_bwd": b * (s * h + 3 * h * ft + 3 * s * ft + s * h) + b * (s * h + 3 * h * ft) + 2 * 2 * b * s * ft,
+        "attn_proj_fwd": b * (s * h + h * (dq + 2 * dkv) + s * dq + dq * h + s * (dq + 2 * dkv) + s * h),
+        "attn_proj_bwd": b * (s * h + h * (dq + 2 * dkv) + s * dq + dq * h + s * (dq + 2 * dkv) + s * h)
+        + b * (s * h + h * (dq + 2 * dkv) + s * dq + dq * h),
+        "attn_core_fwd": b * (s * dq + 2 * s * dkv + s * dq) + 4.0 * nq * s,
+        "attn_core_bwd": b * (3 * s * dq + 2 * s * dkv) + 4.0 * nq * s + b * (s * dq + 2 * s * dkv),
+        "sp_ln_fwd": 9.0 * n_sp * h + 4.0 * h + 8.0 * n_sp,
+        "sp_ln_bwd": 11.0 * n_sp * h + 6.0 * h + 8.0 * n_sp,
+        "lm_head_fwd": b * (s5 * h5 + h5 * Vs) + 4.0 * s5 * Vs,
+        "lm_head_ce_fused": b * (s5 * h5 + h5 * Vs) + 8.0 * s5 + 12.0 * s5,
+        "vocab_ce": 4.0 * s5 * Vs + 20.0 * s5,
+        "vocab_ce_bwd": 6.0 * s5 * Vs + 20.0 * s5,
+        "vocab_embed": 2.0 * s5 * h5 + 2.0 * h5 * s5 / 8 + 8.0 * s5,   # about 1/8 of the ids in the shard
+    }
+    return table[row]
+
+
+def csrc_hash() -> str:
+    names = sorted(n for n in os.listdir(os.path.join(ROOT, "megatron_tensor_layer_tp_amd", "csrc")))
+    return src_hash(*names)
+
+
+def traffic_for(key: str):
+    """HBM bytes per launch of the row's dominant kernel from the committed
+    counter summary, or None when any kernel source changed since the counters
+    were taken."""
     p = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if not os.path.exists(p):
         return None
     with open(p) as f:
         t = json.load(f)
-    e = t.get(kernel_key)
-    if not e or e.get("src_hash") != src_hash(*e["sources"]):
+    if t.get("csrc_hash") != csrc_hash():
         return None
-    return e["bytes_per_launch"]
+    e = t.get("rows", {}).get(key)
+    return e["dominant_kernel"]["bytes"] if e else None
 
 
-# Kernels whose HBM traffic the counter passes measure: summary key -> (pass
-# directory prefix, kernel-name substring, sources the kernel is built from,
-# algorithmic bytes per launch at the V=128256 t=8 vocab shard, s = h = 8192).
-_S5, _H5, _V5 = 8192, 8192, 16032
-TRAFFIC_KERNELS = {
-    "lm_head_gemm": ("lm", "gemm_dma_kernel<256, 256, true, false, 0, true, false, 3>",
-                     ["gemm_bf16_kernels.h", "gemm_bf16.hip", "gemm_desc.h", "launch.h"],
-                     2 * _S5 * _H5 + 2 * _H5 * _V5 + 4 * _S5 * _V5),
-    "lm_head_ce_gemm": ("lmce", "gemm_dma_kernel<256, 256, true, false, 6, true, false, 3>",
-                        ["gemm_bf16_kernels.h", "gemm_bf16.hip", "gemm_desc.h", "launch.h"],
-                        2 * _S5 * _H5 + 2 * _H5 * _V5 + 8 * _S5),
-    "vocab_ce": ("ce", "vocab_ce_kernel<4>", ["vocab.hip"], 4 * _S5 * _V5 + 8 * _S5 + 12 * _S5),
-    "vocab_ce_bwd": ("cebwd", "vocab_ce_bwd_kernel<4, true>", ["vocab.hip"],
-                     4 * _S5 * _V5 + 2 * _S5 * _V5 + 8 * _S5 + 12 * _S5),
-}
-
-
-def summarize_traffic(d: str):
-    """Reduce the rocprofv3 FETCH_SIZE / WRITE_SIZE passes under `d` (one pass
-    per directory <prefix>_<COUNTER>, plus copy_<COUNTER> for the 1 GiB copy)
-    to profiles/hbm_traffic.json: the copy calibrates each counter (bytes per
-    KiB reported), then each kernel's mean counter per dispatch is scaled."""
+def summarize_counters(d: str):
+    """Reduce rocprofv3 --pmc passes under d to profiles/hbm_traffic.json and a
+    markdown table (printed).  Layout: d/<row>/<pass>/**/*counter_collection.csv
+    for each row of ROW_NAMES and pass of COUNTER_PASSES (fetch, write, sq), and
+    d/copy/fetch, d/copy/write for the 1 GiB copy that calibrates FETCH_SIZE and
+    WRITE_SIZE (bytes per KiB reported).  Per (kernel, grid) the counters are
+    averaged over the dispatches after the first (cold caches); kernels launched
+    once per run (the inputs of vocab_ce / attn_core_bwd) are left out."""
     import csv
     import glob
 
-    def mean_counter(prefix, counter, needle):
-        vals = []
-        for f in glob.glob(os.path.join(d, f"{prefix}_{counter}", "**", "*counter_collection.csv"),
-                           recursive=True):
+    def dispatches(path):
+        by = {}
+        for f in glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True):
             with open(f) as fh:
                 for r in csv.DictReader(fh):
-                    if r["Counter_Name"] == counter and needle in r["Kernel_Name"]:
-                        vals.append(float(r["Counter_Value"]))
-        return sum(vals) / len(vals) if vals else None
+                    e = by.setdefault(int(r["Dispatch_Id"]), {"kernel": r["Kernel_Name"], "grid": int(r["Grid_Size"]),
+                                                             "us": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+                                                             / 1000.0})
+                    e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        return [by[k] for k in sorted(by)]
 
-    copy_bytes = 1 << 30
-    cf = mean_counter("copy", "FETCH_SIZE", "copyBuffer")
-    cw = mean_counter("copy", "WRITE_SIZE", "copyBuffer")
-    out = {"calibration": {"copy_bytes": copy_bytes, "fetch_size_kb": cf, "write_size_kb": cw,
-                           "fetch_factor": round(copy_bytes / (cf * 1024), 4),
-                           "write_factor": round(copy_bytes / (cw * 1024), 4)}}
-    ff, wf = copy_bytes / (cf * 1024), copy_bytes / (cw * 1024)
-    for key, (prefix, needle, sources, alg) in TRAFFIC_KERNELS.items():
-        f = mean_counter(prefix, "FETCH_SIZE", needle)
-        w = mean_counter(prefix, "WRITE_SIZE", needle)
-        if f is None or w is None:
+    def per_kernel(recs, counter, runtime=False):
+        groups = {}
+        for e in recs:
+            groups.setdefault((e["kernel"], e["grid"]), []).append(e)
+        out = {}
+        for key, es in groups.items():
+            if len(es) < 2 or (key[0].startswith("__amd_rocclr") and not runtime):  # the inputs' own copies
+                continue
+            es = es[1:]
+            out[key] = {"n": len(es), "us": sum(x["us"] for x in es) / len(es),
+                        counter: sum(x.get(counter, 0.0) for x in es) / len(es)}
+        return out
+
+    def short(name):
+        name = name.replace("void ", "").replace("(anonymous namespace)::", "")
+        return name.split("(GemmDesc")[0].split("((")[0].split("(")[0] if "<" not in name else name.split("(Gemm")[0]
+
+    cf = per_kernel(dispatches(os.path.join(d, "copy", "fetch")), "FETCH_SIZE", runtime=True)
+    cw = per_kernel(dispatches(os.path.join(d, "copy", "write")), "WRITE_SIZE", runtime=True)
+    kf = next(v for k, v in cf.items() if "copyBuffer" in k[0])["FETCH_SIZE"]
+    kw = next(v for k, v in cw.items() if "copyBuffer" in k[0])["WRITE_SIZE"]
+    ff, wf = (1 << 30) / (kf * 1024), (1 << 30) / (kw * 1024)
+    res = {"csrc_hash": csrc_hash(),
+           "calibration": {"copy_bytes": 1 << 30, "fetch_size_kib": round(kf, 1), "write_size_kib": round(kw, 1),
+                           "fetch_factor": round(ff, 4), "write_factor": round(wf, 4)},
+           "rows": {}}
+    lines = ["| row | kernel | grid | us | FETCH KiB | WRITE KiB | HBM bytes | MFMA busy |",
+             "|---|---|---:|---:|---:|---:|---:|---:|"]
+    for row in ROW_NAMES:
+        rd = os.path.join(d, row)
+        if not os.path.isdir(rd):
             continue
-        out[key] = {"kernel": needle, "sources": sources, "src_hash": src_hash(*sources),
-                    "fetch_size_kb": round(f, 1), "write_size_kb": round(w, 1),
-                    "bytes_per_launch": int(f * 1024 * ff + w * 1024 * wf), "algorithmic_bytes": alg}
+        f = per_kernel(dispatches(os.path.join(rd, "fetch")), "FETCH_SIZE")
+        w = per_kernel(dispatches(os.path.join(rd, "write")), "WRITE_SIZE")
+        sq = {}
+        for k, v in per_kernel(dispatches(os.path.join(rd, "sq")), "SQ_VALU_MFMA_BUSY_CYCLES").items():
+            sq[k] = v
+        recs = dispatches(os.path.join(rd, "sq"))
+        busy = {}
+        for e in recs:
+            busy.setdefault((e["kernel"], e["grid"]), []).append(e)
+        kernels = []
+        for key in f:
+            if key not in w:
+                continue
+            by = f[key]["FETCH_SIZE"] * 1024 * ff + w[key]["WRITE_SIZE"] * 1024 * wf
+            mf = None
+            es = busy.get(key, [])[1:]
+            if es:
+                mb = sum(x.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) for x in es)
+                cu = sum(x.get("SQ_BUSY_CU_CYCLES", 0.0) for x in es)
+                mf = mb / (4.0 * cu) if cu > 0 else None
+            kernels.append({"kernel": short(key[0]), "grid": key[1], "us": round(f[key]["us"], 2),
+                            "fetch_kib": round(f[key]["FETCH_SIZE"], 1), "write_kib": round(w[key]["WRITE_SIZE"], 1),
+                            "bytes": int(by), "mfma_busy": None if mf is None else round(mf, 4)})
+        if not kernels:
+            continue
+        dom = max(kernels, key=lambda k: k["us"])
+        total = sum(k["bytes"] for k in kernels)
+        alg = alg_bytes(row)
+        res["rows"][row] = {"kernels": kernels, "dominant_kernel": dom, "bytes_per_call": total,
+                            "algorithmic_bytes": int(alg), "ratio": round(total / alg, 3)}
+        for k in kernels:
+            mfs = "" if k["mfma_busy"] is None else f"{100 * k['mfma_busy']:.1f}%"
+            lines.append(f"| {row} | `{k['kernel']}` | {k['grid']} | {k['us']:.1f} | {k['fetch_kib']:.0f} | "
+                         f"{k['write_kib']:.0f} | {k['bytes'] / 1e6:.1f} MB | {mfs} |")
+        lines.append(f"| {row} | **call total** | | | | | {total / 1e6:.1f} MB "
+                     f"(algorithmic {alg / 1e6:.1f} MB, x{total / alg:.2f}) | |")
     with open(os.path.join(ROOT, "profiles", "hbm_traffic.json"), "w") as fh:
-        json.dump(out, fh, indent=1)
-    print(json.dumps(out, indent=1))
+        json.dump(res, fh, indent=1)
+    print("\n".join(lines))
 
 
 def main():
     args = parse()
-    if args.traffic_summary:
-        summarize_traffic(args.traffic_summary)
+    if args.counter_summary:
+        summarize_counters(args.counter_summary)
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -700,7 +797,7 @@ def main():
         res["roofline"] = {"kernel": "gemm_dma_kernel<256,256,NN,store fp32,8 waves> (tp_lm_head_fwd)",
                            "bound": "mfma", "achieved": round(ach, 2), "peak": PEAK_BF16_TFLOPS,
                            "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4),
-                           "traffic": traffic_for("lm_head_gemm")}
+                           "traffic": traffic_for("lm_head_fwd")}
         c = by["vocab_ce"]
         gbs = c.bytes / (c.ms() * 1e-3) / 1e9
         res["roofline_ce"] = {"kernel": "vocab_ce_kernel<4> (tp_vocab_ce)", "bound": "hbm",
