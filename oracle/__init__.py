@@ -51,7 +51,8 @@ _i64 = ctypes.c_int64
 def _L():
     global _lib
     if _lib is None:
-        lib = ctypes.CDLL(build())
+        # ORACLE_LIB: an alternative build of oracle.c (the sanitizer test's)
+        lib = ctypes.CDLL(os.environ.get("ORACLE_LIB") or build())
         lib.or_gemm.argtypes = [_i64, _i64, _i64, _d, _d, _d]
         lib.or_act.argtypes = [ctypes.c_int, _i64, _d, _d]
         lib.or_act_grad.argtypes = [ctypes.c_int, _i64, _d, _d]
