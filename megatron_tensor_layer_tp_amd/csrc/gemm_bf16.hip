@@ -6,7 +6,7 @@ namespace {
 
 template <int BM, int BN, bool A_KC, bool B_KC, int EPI, bool OUT_F32, bool KSEG, int RES>
 hipError_t launch_dma(const GemmDesc &d, hipStream_t st) {
-  const int nblk = d.tiles_m * d.tiles_n * d.splits;
+  const int nblk = d.nblocks > 0 ? d.nblocks : d.tiles_m * d.tiles_n * d.splits;
   if (nblk == 0) return hipSuccess;
   hipLaunchKernelGGL((gemm_dma_kernel<BM, BN, A_KC, B_KC, EPI, OUT_F32, KSEG, RES>), dim3(nblk),
                      dim3(64 * res_waves(RES)), 0, st, d);
@@ -20,7 +20,7 @@ hipError_t launch_dma(const GemmDesc &d, hipStream_t st) {
 template <bool A_KC, bool B_KC, int EPI, bool OUT_F32, bool KSEG>
 hipError_t launch_shape_k(const GemmDesc &d, int bm, int bn, int res, hipStream_t st, bool vec) {
   if (!vec) {  // element-wise loads (odd sizes / leading dimensions): 128x128 tiles only
-    const int nblk = d.tiles_m * d.tiles_n * d.splits;
+    const int nblk = d.nblocks > 0 ? d.nblocks : d.tiles_m * d.tiles_n * d.splits;
     if (nblk == 0) return hipSuccess;
     hipLaunchKernelGGL((gemm_bf16_kernel<128, 128, A_KC, B_KC, EPI, OUT_F32, false, KSEG>), dim3(nblk),
                        dim3(NTHREADS), 0, st, d);

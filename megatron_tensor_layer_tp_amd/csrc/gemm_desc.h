@@ -59,6 +59,8 @@ struct GemmDesc {
   int32_t group_m;                 // tile-rows per L2 group
   int64_t vstart;                  // EPI_CE_STATS: global id of column 0
   int32_t stream_out;              // bf16 outputs stored non-temporally: bit 0 C, bit 1 ao0, bit 2 ao1
+  int32_t nblocks;                 // > 0: launch only logical blocks [0, nblocks) (a prefix of the
+                                   // tile order); 0: all tiles_m * tiles_n * splits
 };
 
 // ---------------------------------------------------------------------------

@@ -425,17 +425,139 @@ GemmVariant variant(const Spec &s, const Plan &p) {
   return v;
 }
 
+// Host replica of the kernels' logical tile order (tile_of, group_m tile rows
+// per group, columns within a group): logical tile t -> (tile row, tile column).
+void tile_rc(int tiles_m, int tiles_n, int group_m, int t, int &tm, int &tn) {
+  const int in_group = group_m * tiles_n;
+  const int g = t / in_group;
+  const int first = g * group_m;
+  const int gsz = std::min(tiles_m - first, group_m);
+  const int w = t - g * in_group;
+  tm = first + w % gsz;
+  tn = w / gsz;
+}
+
+// The last round of a launch that fills at most half the workgroup slots,
+// re-tiled: the first launch runs only the whole rounds (a prefix of the tile
+// order: the kernels map block ids onto [0, grid)), and the remaining tiles,
+// when they form a rectangle of the output, run as a product of their own
+// with the tile shape the planner picks for that sub-matrix (smaller tiles
+// spread it over all the slots).  Same epilogue, same K, no workspace.
+struct Tail {
+  bool on = false;
+  int head = 0;                 // blocks of the first launch
+  int64_t r0 = 0, c0 = 0;       // first output row and column of the rectangle
+  Spec sub;
+  Plan p;
+};
+
+// TP_GEMM_TAIL=off never re-tiles a last round; =force re-tiles it whenever it
+// is a rectangle of at most half the slots, whatever the cost model says (the
+// parity tests use it to run the path at small sizes); unset: the cost model decides.
+int tail_mode() {
+  const char *e = std::getenv("TP_GEMM_TAIL");
+  if (e == nullptr) return 0;
+  if (std::strcmp(e, "off") == 0) return -1;
+  if (std::strcmp(e, "force") == 0) return 1;
+  return 0;
+}
+
+Tail plan_tail(const Spec &s, const Plan &p) {
+  Tail t;
+  const int mode = tail_mode();
+  if (mode < 0 || !p.vec || p.splits != 1 || s.nseg != 1 || s.kseg || s.epi == EPI_CE_STATS) return t;
+  const int T = p.tiles_m * p.tiles_n, S = plan_slots(p);
+  const int rem = T % S;
+  if (T <= S || rem == 0 || 2 * rem > S) return t;
+  int a = p.tiles_m, b = -1, c = p.tiles_n, e = -1;
+  for (int i = T - rem; i < T; ++i) {
+    int tm, tn;
+    tile_rc(p.tiles_m, p.tiles_n, 8, i, tm, tn);
+    a = std::min(a, tm);
+    b = std::max(b, tm);
+    c = std::min(c, tn);
+    e = std::max(e, tn);
+  }
+  if ((int64_t)(b - a + 1) * (e - c + 1) != rem) return t;
+  const int ncols = s.dual ? p.bn / 2 : p.bn;
+  Spec sub = s;
+  sub.can_split = false;
+  sub.M = std::min<int64_t>((int64_t)(b + 1) * p.bm, s.M) - (int64_t)a * p.bm;
+  sub.N = std::min<int64_t>((int64_t)(e + 1) * ncols, s.seg[0]) - (int64_t)c * ncols;
+  sub.seg[0] = sub.N;
+  const Plan p2 = plan_bf16(sub);
+  if (!p2.vec || p2.splits != 1) return t;
+  const int head = T - rem;
+  const double head_us = kLaunchUs + tile_cost(p.bm, p.bn, p.res).first + (double)(head / S) * block_us(s, p, head);
+  if (mode == 0 && head_us + plan_us(sub, p2) >= 0.98 * plan_us(s, p)) return t;
+  t.on = true;
+  t.head = head;
+  t.r0 = (int64_t)a * p.bm;
+  t.c0 = (int64_t)c * ncols;
+  t.sub = sub;
+  t.p = p2;
+  return t;
+}
+
+// the operand and output pointers of the sub-matrix at (r0, c0) of a product
+Ptrs offset_ptrs(const Spec &s, const Ptrs &q, int64_t r0, int64_t c0) {
+  Ptrs o = q;
+  const int64_t cb = s.out_f32 ? 4 : 2;
+  auto adv = [](const void *p, int64_t bytes) { return (const void *)((const char *)p + bytes); };
+  o.A[0] = adv(q.A[0], 2 * (s.layout == GEMM_TN ? r0 : r0 * q.lda[0]));
+  for (int i = 0; i < (s.dual ? 2 : 1); ++i)
+    o.B[i] = adv(q.B[i], 2 * (s.layout == GEMM_NT ? c0 * q.ldb[i] : c0));
+  o.C[0] = (void *)adv(q.C[0], cb * (r0 * q.ldc[0] + c0));
+  if (q.ai0) o.ai0 = adv(q.ai0, 2 * (r0 * q.ldai + c0));
+  if (q.ai1) o.ai1 = adv(q.ai1, 2 * (r0 * q.ldai + c0));
+  if (q.ao0) o.ao0 = (void *)adv(q.ao0, 2 * (r0 * q.ldao + c0));
+  if (q.ao1) o.ao1 = (void *)adv(q.ao1, 2 * (r0 * q.ldao + c0));
+  return o;
+}
+
+// TP_PLAN_LOG=1: one line per launch on stderr with the plan the cost model chose
+bool plan_log() {
+  static const bool on = [] {
+    const char *e = std::getenv("TP_PLAN_LOG");
+    return e != nullptr && *e != 0 && *e != '0';
+  }();
+  return on;
+}
+const char *res_name(int res) {
+  return res == RES_TWO ? "two" : res == RES_THREE ? "three" : res == RES_SHARED ? "shared" : "waves8";
+}
+void log_plan(const char *what, const Spec &s, const Plan &p, const char *extra = "") {
+  if (!plan_log()) return;
+  std::fprintf(stderr, "[tp plan] %s: M=%lld N=%lld K=%lld %dx%d:%s tiles=%dx%d splits=%d%s%s\n", what,
+               (long long)s.M, (long long)s.N, (long long)s.K, p.bm, p.bn, res_name(p.res), p.tiles_m, p.tiles_n,
+               p.splits, p.vec ? "" : " (element-wise loads)", extra);
+}
+
 int run_planned(const Spec &s, const Plan &p, const Ptrs &q, int dt, void *ws, hipStream_t st,
                 const char *what) {
   if (p.splits > 1 && ws == nullptr) return fail(TP_EWORKSPACE, "%s: split-K plan without workspace", what);
-  const GemmDesc d = make_desc(s, q, p, dt, ws);
+  GemmDesc d = make_desc(s, q, p, dt, ws);
   hipError_t e;
   if (dt == TP_DT_F32) {
     e = tp_launch_gemm_f32(d, s.layout, s.epi, st);
   } else {
+    const Tail tail = plan_tail(s, p);
+    if (tail.on) d.nblocks = tail.head;
+    if (plan_log()) {
+      char extra[160] = "";
+      if (tail.on)
+        std::snprintf(extra, sizeof extra, "; first %d blocks, then rows %lld.. cols %lld.. (%lldx%lld) as %dx%d:%s",
+                      tail.head, (long long)tail.r0, (long long)tail.c0, (long long)tail.sub.M,
+                      (long long)tail.sub.N, tail.p.bm, tail.p.bn, res_name(tail.p.res));
+      log_plan(what, s, p, extra);
+    }
     const GemmVariant v = variant(s, p);
     e = tp_launch_gemm_bf16(d, v, st);
     if (e == hipSuccess && p.splits > 1) e = tp_launch_splitk_reduce(d, s.out_f32, p.vec, st);
+    if (e == hipSuccess && tail.on) {
+      const GemmDesc d2 = make_desc(tail.sub, offset_ptrs(s, q, tail.r0, tail.c0), tail.p, dt, nullptr);
+      e = tp_launch_gemm_bf16(d2, variant(tail.sub, tail.p), st);
+    }
   }
   if (e != hipSuccess) return fail(TP_EHIP, "%s: %s", what, hipGetErrorString(e));
   return TP_OK;
@@ -466,6 +588,9 @@ PairPlan pair_plan(const Spec &s1, const Spec &s2, int dt) {
   r.p1 = plan_bf16(s1);
   r.p2 = plan_bf16(s2);
   double best = plan_us(s1, r.p1) + plan_us(s2, r.p2);
+  // TP_GEMM_PAIR=off: always apart (timing comparisons; the parity tests use it
+  // to reach the single-launch paths of products that are normally paired)
+  if (const char *e = std::getenv("TP_GEMM_PAIR"); e != nullptr && std::strcmp(e, "off") == 0) return r;
   // together: every built pair of variants with one residency, the first
   // possibly split along K
   Spec b = s2;
@@ -529,6 +654,8 @@ int run_pair(const Spec &s1, const Ptrs &q1, const Spec &s2, const Ptrs &q2, int
     return run_planned(s2, pp.p2, q2, dt, ws, st, what2);
   }
   if (pp.p1.splits > 1 && ws == nullptr) return fail(TP_EWORKSPACE, "%s: split-K plan without workspace", what1);
+  log_plan(what1, s1, pp.p1, " (paired, first)");
+  log_plan(what2, s2, pp.p2, " (paired, second)");
   const GemmDesc d1 = make_desc(s1, q1, pp.p1, dt, ws);
   const GemmDesc d2 = make_desc(s2, q2, pp.p2, dt, nullptr);
   hipError_t e = tp_launch_gemm_pair(d1, variant(s1, pp.p1), d2, variant(s2, pp.p2), red, false, st);
