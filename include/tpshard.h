@@ -308,8 +308,9 @@ int tp_vocab_ce_bwd(int dt, int64_t s, int64_t Vs, int64_t vocab_start,
  * fp32 rounding).  Hf [s,h], Wlm [h,Vs], target [s] global ids; dt must be
  * TP_DT_BF16 (TP_EUNSUPPORTED otherwise).  ws: device scratch of at least
  * tp_lm_head_ce_workspace(dt, s, h, Vs) bytes, 256-byte aligned, overwritten
- * (per-position partial statistics of every column block, about
- * 12 * s * Vs / 128 bytes). */
+ * (per-position max and sum of exponentials of every column block of the
+ * GEMM's tiling, plus the target logit: 4 * s * (2 * ceil(Vs / BN) + 1) bytes,
+ * BN the tile width the call's plan takes, 128 or 256). */
 size_t tp_lm_head_ce_workspace(int dt, int64_t s, int64_t h, int64_t Vs);
 int tp_lm_head_ce_fwd(int dt, int64_t s, int64_t h, int64_t Vs, int64_t vocab_start,
                       const void *Hf, const void *Wlm, const int64_t *target,
@@ -320,8 +321,8 @@ int tp_lm_head_ce_fwd(int dt, int64_t s, int64_t h, int64_t Vs, int64_t vocab_st
  * cannot allocate device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc).  The per-part statistics go to a
  * scratch array the library holds on each GPU it runs on, of
- * tp_lm_head_ce_noalloc_max_bytes() = 32 MiB (enough for s * Vs up to about
- * 2.8e6 * 256 / 12, e.g. s = 8192 positions of a 16032-wide vocab shard):
+ * tp_lm_head_ce_noalloc_max_bytes() = 32 MiB (with 256-wide tiles enough for
+ * s * Vs up to about 1e9, e.g. s = 65536 positions of a 16032-wide shard):
  * larger requests return TP_EWORKSPACE before anything is enqueued.  The call
  * allocates nothing (no hipMalloc, hipFree or allocating library routine).
  * The stream must belong to the current device.  Every call on one GPU shares

@@ -340,16 +340,16 @@ __device__ __forceinline__ float row_sum(float v) {
 
 // Cross-entropy statistics of the LM head's logits without storing them
 // (lecture 16 notes §5.5, the fused vocab-parallel cross entropy): the LPR
-// lanes holding row gm's columns of one wave's half-tile (8 each, from gn)
-// reduce them to the row's max over the valid columns and the sum of
-// exp(z - max); the lane holding the target id's column (if any) records its
-// logit.  Partials go to ws[gm][k][part] (k = max, sum, target logit; part =
-// this half-tile's index); the target slot is written only by the part that
-// holds the target.  Every lane must call it (cross-lane moves); rows >= M
-// write nothing.
+// lanes holding row gm's columns of one wave's strip (8 each, from gn) reduce
+// them to the row's max over the valid columns (mx) and the sum of
+// exp(z - max) (se); every one of them gets both.  The lane holding the target
+// id's column (if any; over the whole launch exactly one lane holds it)
+// stores that logit to tl[gm], read back from the LDS strip src that x was
+// loaded from (an index into x itself would put x in scratch memory).  Every
+// lane must call it (cross-lane moves); rows >= M store nothing.
 template <int LPR>
-__device__ __forceinline__ void ce_stats8(const GemmDesc &d, int gm, int gn, int nlen, int part, int P, int lane,
-                                          const float *x) {
+__device__ __forceinline__ void ce_row8(const GemmDesc &d, int gm, int gn, int nlen, const float *x,
+                                        const float *src, float *tl, float &mx_out, float &se_out) {
   static_assert(LPR == 8 || LPR == 16, "row reductions span 8 or 16 lanes");
   constexpr float LOG2E = 1.4426950408889634f;
   const int nv = min(8, nlen - gn);  // valid columns of this lane (may be <= 0)
@@ -365,21 +365,43 @@ __device__ __forceinline__ void ce_stats8(const GemmDesc &d, int gm, int gn, int
     for (int q = 0; q < 8; ++q)
       if (q < nv) se += tp_exp2(fmaf(x[q], LOG2E, -mb));
   }
-  se = row_sum<LPR>(se);
+  mx_out = mx;
+  se_out = row_sum<LPR>(se);
   if (gm < d.M) {
-    float *w = d.ws + (int64_t)gm * 3 * P + part;
-    if (lane % LPR == 0) {
-      w[0] = mx;
-      w[P] = se;
-    }
     const int64_t j = ((const int64_t *)d.ai0)[gm] - d.vstart - gn;
-    if (j >= 0 && j < nv) {
-      float t = x[0];
+    if (j >= 0 && j < nv) tl[gm] = src[j];
+  }
+}
+
+// The NC wave columns' statistics of each of the tile's BM rows (red[j*BM + r]
+// = max, red[(NC + j)*BM + r] = sum of exp(z - max), j = wave column) merged in
+// column order -- M = max_j m_j, S = sum_j s_j exp(m_j - M), the combine the
+// per-row merge across tiles repeats -- and stored as tile column tc's part:
+// ws[tc][gm] = M, ws[P + tc][gm] = S (P = tiles_n, rows of length d.M), so a
+// tile stores two runs of BM consecutive floats.  Every thread must call it
+// (workgroup barrier).
+template <int BM, int NC, int NT>
+__device__ __forceinline__ void ce_tile_merge(const GemmDesc &d, const float *red, int m0, int tc) {
+  static_assert(NT >= BM, "one thread per row of the tile");
+  constexpr float LOG2E = 1.4426950408889634f;
+  __syncthreads();
+  const int t = threadIdx.x, gm = m0 + t;
+  if (t < BM && gm < d.M) {
+    float mx = -INFINITY;
 #pragma unroll
-      for (int q = 1; q < 8; ++q)
-        if (j == q) t = x[q];
-      w[2 * P] = t;
+    for (int j = 0; j < NC; ++j) mx = fmaxf(mx, red[j * BM + t]);
+    float se = 0.f;
+    if (mx != -INFINITY) {
+      const float mb = mx * LOG2E;
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        const float mj = red[j * BM + t];
+        if (mj != -INFINITY) se += red[(NC + j) * BM + t] * tp_exp2(fmaf(mj, LOG2E, -mb));
+      }
     }
+    float *w = d.ws + (int64_t)tc * d.M + gm;
+    w[0] = mx;
+    w[(int64_t)d.tiles_n * d.M] = se;
   }
 }
 
@@ -436,7 +458,8 @@ __device__ __forceinline__ void epilogue_f32_direct(const GemmDesc &d, f32x16 (&
 
 template <int BM, int BN, int EPI, bool OUT_F32, bool VEC, bool DUAL, int NW = 4>
 __device__ __forceinline__ void epilogue(const GemmDesc &d, f32x16 (&acc)[BM / 64][2 * BN / NW / 32], float *ep,
-                                         int lane, int wm, int wn, int m0, int n0, int nlen, int sc, int split) {
+                                         int lane, int wm, int wn, int m0, int n0, int nlen, int sc, int split,
+                                         float *red = nullptr) {
   constexpr int WTM = BM / 2, WTN = BN / (NW / 2), FM = WTM / 32, FN = WTN / 32;
   constexpr int EPS = WTN + 8;                      // strip row stride (floats)
   constexpr int OUTW = DUAL ? WTN / 2 : WTN;        // output columns per strip row
@@ -501,14 +524,21 @@ __device__ __forceinline__ void epilogue(const GemmDesc &d, f32x16 (&acc)[BM / 6
       const int gm = m0 + wm * WTM + fm * 32 + r;
       const int gn = col_base + c;
       if constexpr (EPI == EPI_CE_STATS) {
-        // one part per wave column of every tile: BN / WTN parts per tile
-        ce_stats8<LPR>(d, gm, gn, nlen, col_base / WTN, (BN / WTN) * d.tiles_n, lane, x);
+        // per row of the strip: this wave column's statistics into red (LDS)
+        float mx, se;
+        ce_row8<LPR>(d, gm, gn, nlen, x, src, d.ws + (int64_t)2 * d.tiles_n * d.M, mx, se);
+        if (lane % LPR == 0) {
+          const int rt = wm * WTM + fm * 32 + r;
+          red[wn * BM + rt] = mx;
+          red[(NW / 2 + wn) * BM + rt] = se;
+        }
       } else {
         if (live && gm < d.M && gn < nlen)
           epi8<EPI, OUT_F32, VEC>(d, gm, gn, nlen, sc, split, x, u, PRE ? pre[PRE ? it : 0] : nullptr);
       }
     }
   }
+  if constexpr (EPI == EPI_CE_STATS) ce_tile_merge<BM, NW / 2, 64 * NW>(d, red, m0, n0 / BN);
 }
 
 template <int BM, int BN>
@@ -670,7 +700,10 @@ __global__ void __launch_bounds__(NTHREADS) gemm_bf16_kernel(GemmDesc d) {
   }
 
   float *ep = (float *)&sm + wid * 32 * (WTN + 8);
-  epilogue<BM, BN, EPI, OUT_F32, VEC, DUAL>(d, acc, ep, lane, wm, wn, m0, n0, nlen, KSEG ? 0 : sn, split);
+  // CE statistics: the per-row merge buffer sits after the 4 waves' strips
+  static_assert(EPI != EPI_CE_STATS || 4 * (4 * 32 * (WTN + 8) + 4 * BM) <= (int)sizeof(sm), "CE buffer");
+  epilogue<BM, BN, EPI, OUT_F32, VEC, DUAL>(d, acc, ep, lane, wm, wn, m0, n0, nlen, KSEG ? 0 : sn, split,
+                                            (float *)&sm + 4 * 32 * (WTN + 8));
 }
 
 // ===========================================================================
@@ -1105,7 +1138,10 @@ __device__ __forceinline__ void dma_body(const GemmDesc &d, int lid, char *smem0
     epilogue_f32_direct<BM, BN, NW, EPI == EPI_PARTIAL>(d, acc, lane, wm, wn, m0, n0, nlen, KSEG ? 0 : sn, split);
     return;
   }
-  epilogue<BM, BN, EPI, OUT_F32, true, DUAL, NW>(d, acc, ep, lane, wm, wn, m0, n0, nlen, KSEG ? 0 : sn, split);
+  // CE statistics: the per-row merge buffer sits in stage 0 after the first half's strips
+  static_assert(EPI != EPI_CE_STATS || 4 * ((NW / 2) * 32 * (WTN + 8) + NW * BM) <= 128 * (BM + BN), "CE buffer");
+  epilogue<BM, BN, EPI, OUT_F32, true, DUAL, NW>(d, acc, ep, lane, wm, wn, m0, n0, nlen, KSEG ? 0 : sn, split,
+                                                 (float *)smem0 + (NW / 2) * 32 * (WTN + 8));
 }
 
 // Sum the split-K partials in split order (deterministic) and store.  Each

@@ -26,8 +26,8 @@ enum EpiKind : int {
   EPI_SWIGLU_FWD = 3,  // dual: ao0 = g, ao1 = u, C = SiLU(g) * u
   EPI_SWIGLU_BWD = 4,  // C = acc * ai1 * SiLU'(ai0) (dG); ao0 = acc * SiLU(ai0) (dU)
   EPI_PARTIAL = 5,     // fp32 split-K partial into ws[split][M][N]
-  EPI_CE_STATS = 6,    // logits stay on chip: per row and per wave column of a tile
-                       // (P parts in all), (max, sum exp(z - max), target logit) into ws[M][3][P]
+  EPI_CE_STATS = 6,    // logits stay on chip: per row and tile column (P = tiles_n parts),
+                       // max into ws[P][M], sum exp(z - max) into ws[P + p][M], target logit ws[2P][M]
 };
 
 enum ActKind : int { ACT_RELU = 0, ACT_GELU = 1 };

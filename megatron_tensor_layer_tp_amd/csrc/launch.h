@@ -27,7 +27,6 @@ constexpr int res_stages(int res) { return res == RES_THREE ? 3 : 2; }
 constexpr int res_wgs(int res) { return res == RES_SHARED ? 2 : 1; }
 constexpr int res_waves(int res) { return res == RES_WAVES8 ? 8 : 4; }
 // columns of one wave's sub-tile (the waves form a 2 x waves/2 grid)
-constexpr int res_wave_cols(int bn, int res) { return bn / (res_waves(res) / 2); }
 constexpr bool res_fits(int bm, int bn, int res) {
   return res_stages(res) * res_wgs(res) * 128 * (bm + bn) <= 160 * 1024;
 }
@@ -69,9 +68,10 @@ hipError_t tp_launch_vocab_ce(int64_t s, int64_t Vs, int64_t start, const float 
 hipError_t tp_launch_vocab_ce_bwd(bool bf16_out, int64_t s, int64_t Vs, int64_t start, const float *z,
                                   const int64_t *tgt, const float *M, const float *S, const float *g, void *out,
                                   hipStream_t st);
-// merge the fused LM-head GEMM's per-part CE statistics ws [s][3][P] (parts of W columns)
-hipError_t tp_launch_ce_merge(const float *ws, int P, int W, int64_t s, int64_t Vs, int64_t start,
-                              const int64_t *tgt, float *m, float *se, float *tl, hipStream_t st);
+// merge the fused LM-head GEMM's per-tile-column CE statistics: ws = max [P][s], sum exp [P][s],
+// target logit [s]
+hipError_t tp_launch_ce_merge(const float *ws, int P, int64_t s, int64_t Vs, int64_t start, const int64_t *tgt,
+                              float *m, float *se, float *tl, hipStream_t st);
 hipError_t tp_launch_vocab_embed(int elem_bytes, int64_t n, int64_t Vs, int64_t h, int64_t start,
                                  const int64_t *ids, const void *table, void *out, hipStream_t st);
 

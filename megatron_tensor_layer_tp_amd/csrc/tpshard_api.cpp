@@ -814,7 +814,7 @@ AttnBwdLayout attn_bwd_layout(int dt, int64_t s, int64_t h, int64_t dq, int64_t 
 struct LmCePlan {
   Spec g;
   Plan p;
-  int parts = 0, width = 0;
+  int parts = 0;
   size_t bytes = 0;
 };
 LmCePlan lm_ce_plan(int64_t s, int64_t h, int64_t Vs) {
@@ -822,9 +822,8 @@ LmCePlan lm_ce_plan(int64_t s, int64_t h, int64_t Vs) {
   L.g = spec_nn(s, Vs, h, EPI_CE_STATS);
   L.g.out_f32 = true;
   L.p = plan_bf16(L.g);
-  L.width = res_wave_cols(L.p.bn, L.p.res);  // one part per wave column of a tile
-  L.parts = L.p.tiles_n * (L.p.bn / L.width);
-  L.bytes = align256((size_t)s * 3 * L.parts * sizeof(float));
+  L.parts = L.p.tiles_n;  // one part per tile column: max [parts][s], sum exp [parts][s], target logit [s]
+  L.bytes = align256((size_t)s * (2 * (size_t)L.parts + 1) * sizeof(float));
   return L;
 }
 
@@ -1440,8 +1439,7 @@ int lm_ce_launch(const LmCePlan &L, int64_t s, int64_t h, int64_t Vs, int64_t vo
   d.vstart = vocab_start;
   hipError_t e = tp_launch_gemm_bf16(d, variant(L.g, L.p), st);
   if (e == hipSuccess)
-    e = tp_launch_ce_merge((const float *)ws, L.parts, L.width, s, Vs, vocab_start, target, lmax, lsumexp, tlogit,
-                           st);
+    e = tp_launch_ce_merge((const float *)ws, L.parts, s, Vs, vocab_start, target, lmax, lsumexp, tlogit, st);
   if (e != hipSuccess) return fail(TP_EHIP, "%s: %s", call, hipGetErrorString(e));
   return ok();
 }

@@ -151,59 +151,48 @@ __global__ void __launch_bounds__(CE_THREADS) vocab_ce_bwd_kernel(const float *_
   }
 }
 
-// Merge the per-half-tile statistics of the fused LM-head GEMM into the
-// shard's three numbers per position: one wave per row reads its P partials
-// ws[row][k][p] (k = max, sum exp, target logit), takes M = max_p m_p and
-// S = sum_p se_p exp(m_p - M) in a fixed order, and picks the target's logit
-// from the part of width W that holds column target - start.
-__global__ void __launch_bounds__(256) ce_merge_kernel(const float *__restrict__ ws, int P, int W, int64_t s,
+// Merge the per-tile-column statistics of the fused LM-head GEMM into the
+// shard's three numbers per position.  ws holds P parts per row, part-major:
+// ws[p][row] = the max over tile column p, ws[P + p][row] = the sum of
+// exp(z - that max), and ws[2P][row] = the target's logit (written by the
+// tile that holds column target - start).  A workgroup takes 64 rows, one per
+// lane, so every load is a run of 64 consecutive floats; its 4 waves split the
+// parts (wave q: p = q, q + 4, ...) and their results combine in wave order:
+// M = max_p m_p, S = sum_p se_p exp(m_p - M).
+__global__ void __launch_bounds__(256) ce_merge_kernel(const float *__restrict__ ws, int P, int64_t s,
                                                        int64_t Vs, int64_t start,
                                                        const int64_t *__restrict__ tgt,
                                                        float *__restrict__ m_out, float *__restrict__ se_out,
                                                        float *__restrict__ tl_out) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= s) return;
-  const float *w = ws + row * 3 * (int64_t)P;
-  const int64_t y = tgt[row];
-  const bool own = y >= start && y - start < Vs;
-  float tl = 0.f;
-  if (lane == 0 && own) tl = w[2 * P + (y - start) / W];  // in flight with the partials
-  float mx = -INFINITY, sum = 0.f;
-  constexpr int U = 4;
-  if (P <= 64 * U) {  // every partial of the row in registers, loaded in one batch
-    float mv[U], sv[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int p = u * 64 + lane;
-      mv[u] = p < P ? w[p] : -INFINITY;
-      sv[u] = p < P ? w[P + p] : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) mx = fmaxf(mx, mv[u]);
-    mx = wave_max(mx);
-    if (mx != -INFINITY) {
-      const float mb = mx * LOG2E;
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (mv[u] != -INFINITY) sum += sv[u] * exp2f(fmaf(mv[u], LOG2E, -mb));
-    }
-  } else {
-    for (int p = lane; p < P; p += 64) mx = fmaxf(mx, w[p]);
-    mx = wave_max(mx);
-    if (mx != -INFINITY) {
-      const float mb = mx * LOG2E;
-      for (int p = lane; p < P; p += 64) {
-        const float mp = w[p];
-        if (mp != -INFINITY) sum += w[P + p] * exp2f(fmaf(mp, LOG2E, -mb));
-      }
+  __shared__ float part[2][4][64];
+  const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * 64 + lane;
+  const bool live = row < s;
+  const float *wm = ws + row, *wse = ws + (int64_t)P * s + row;
+  float mx = -INFINITY;
+  if (live) {
+#pragma unroll 8
+    for (int p = q; p < P; p += 4) mx = fmaxf(mx, wm[(int64_t)p * s]);
+  }
+  part[0][q][lane] = mx;
+  __syncthreads();
+  const float M = fmaxf(fmaxf(part[0][0][lane], part[0][1][lane]), fmaxf(part[0][2][lane], part[0][3][lane]));
+  float sum = 0.f;
+  if (live && M != -INFINITY) {
+    const float mb = M * LOG2E;
+#pragma unroll 8
+    for (int p = q; p < P; p += 4) {
+      const float mp = wm[(int64_t)p * s];
+      if (mp != -INFINITY) sum += wse[(int64_t)p * s] * exp2f(fmaf(mp, LOG2E, -mb));
     }
   }
-  sum = wave_sum(sum);
-  if (lane == 0) {
-    m_out[row] = mx;
-    se_out[row] = sum;
-    tl_out[row] = tl;
+  part[1][q][lane] = sum;
+  __syncthreads();
+  if (q == 0 && live) {
+    const int64_t y = tgt[row];
+    m_out[row] = M;
+    se_out[row] = ((part[1][0][lane] + part[1][1][lane]) + part[1][2][lane]) + part[1][3][lane];
+    tl_out[row] = (y >= start && y - start < Vs) ? ws[(int64_t)2 * P * s + row] : 0.f;
   }
 }
 
@@ -243,11 +232,11 @@ hipError_t tp_launch_vocab_ce(int64_t s, int64_t Vs, int64_t start, const float 
   return hipGetLastError();
 }
 
-hipError_t tp_launch_ce_merge(const float *ws, int P, int W, int64_t s, int64_t Vs, int64_t start,
-                              const int64_t *tgt, float *m, float *se, float *tl, hipStream_t st) {
+hipError_t tp_launch_ce_merge(const float *ws, int P, int64_t s, int64_t Vs, int64_t start, const int64_t *tgt,
+                              float *m, float *se, float *tl, hipStream_t st) {
   if (s == 0) return hipSuccess;
-  hipLaunchKernelGGL(ce_merge_kernel, dim3((unsigned)((s + 3) / 4)), dim3(256), 0, st, ws, P, W, s, Vs, start,
-                     tgt, m, se, tl);
+  hipLaunchKernelGGL(ce_merge_kernel, dim3((unsigned)((s + 63) / 64)), dim3(256), 0, st, ws, P, s, Vs, start, tgt,
+                     m, se, tl);
   return hipGetLastError();
 }
 

@@ -123,8 +123,8 @@ def test_layer_calls_validation(L):
 
 def test_lm_head_ce_validation(L):
     need = T.tp_lm_head_ce_workspace(T.TP_DT_BF16, 8192, 8192, 16032)
-    # three fp32 partials per position for every half-tile of columns
-    assert need >= 8192 * 3 * 4 * (2 * (16032 // 256))
+    # two fp32 partials per position for every tile column (at most 256 wide), plus the target logit
+    assert need >= 8192 * 4 * (2 * (16032 // 256) + 1)
     assert need == T.tp_lm_head_ce_workspace(T.TP_DT_BF16, 8192, 8192, 16032)
     assert T.tp_lm_head_ce_workspace(T.TP_DT_F32, 8, 8, 8) == 0
     args = [T.TP_DT_BF16, 8192, 8192, 16032, 0] + [A16] * 6
@@ -274,8 +274,8 @@ def test_lm_head_ce_noalloc_validation(L):
     assert _st(L, "tp_lm_head_ce_fwd_noalloc", *bad) == T.TP_EINVAL
     # beyond the scratch: refused before anything is enqueued
     bad = list(args)
-    bad[1] = 16384
-    assert T.tp_lm_head_ce_workspace(T.TP_DT_BF16, 16384, 8192, 16032) > cap
+    bad[1], bad[3] = 65536, 32064
+    assert T.tp_lm_head_ce_workspace(T.TP_DT_BF16, 65536, 8192, 32064) > cap
     assert _st(L, "tp_lm_head_ce_fwd_noalloc", *bad) == T.TP_EWORKSPACE
     assert "scratch" in T.tp_last_error()
     # nothing to compute: no positions (no device touched)

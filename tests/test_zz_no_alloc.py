@@ -63,7 +63,7 @@ def test_noalloc_matches_workspace_call_twice():
 def test_noalloc_refuses_more_than_its_scratch():
     cap = T.tp_lm_head_ce_noalloc_max_bytes()
     assert cap == 32 << 20
-    s, h, Vs = 16384, 64, 16032     # 16384 * 3 * 252 * 4 bytes > 32 MiB
+    s, h, Vs = 65536, 64, 32064     # at least 65536 * (2 * 126 + 1) * 4 bytes > 32 MiB
     assert T.tp_lm_head_ce_workspace(BF, s, h, Vs) > cap
     A = torch.empty(16, dtype=torch.int16, device="cuda:0")
     with pytest.raises(T.TpError) as e:
