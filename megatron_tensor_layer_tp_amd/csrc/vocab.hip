@@ -158,20 +158,32 @@ __global__ void __launch_bounds__(CE_THREADS) vocab_ce_bwd_kernel(const float *_
 // tile that holds column target - start).  A workgroup takes 64 rows, one per
 // lane, so every load is a run of 64 consecutive floats; its 4 waves split the
 // parts (wave q: p = q, q + 4, ...) and their results combine in wave order:
-// M = max_p m_p, S = sum_p se_p exp(m_p - M).
+// M = max_p m_p, S = sum_p se_p exp(m_p - M).  Up to 4 * 16 parts per row all
+// loads of a thread are in flight at once (one memory round trip).
 __global__ void __launch_bounds__(256) ce_merge_kernel(const float *__restrict__ ws, int P, int64_t s,
                                                        int64_t Vs, int64_t start,
                                                        const int64_t *__restrict__ tgt,
                                                        float *__restrict__ m_out, float *__restrict__ se_out,
                                                        float *__restrict__ tl_out) {
+  constexpr int U = 16;
   __shared__ float part[2][4][64];
   const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
   const int64_t row = (int64_t)blockIdx.x * 64 + lane;
   const bool live = row < s;
   const float *wm = ws + row, *wse = ws + (int64_t)P * s + row;
+  float mv[U], sv[U];
   float mx = -INFINITY;
-  if (live) {
-#pragma unroll 8
+  if (P <= 4 * U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p = q + 4 * u;
+      const bool ok = live && p < P;
+      mv[u] = ok ? wm[(int64_t)p * s] : -INFINITY;
+      sv[u] = ok ? wse[(int64_t)p * s] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) mx = fmaxf(mx, mv[u]);
+  } else if (live) {
     for (int p = q; p < P; p += 4) mx = fmaxf(mx, wm[(int64_t)p * s]);
   }
   part[0][q][lane] = mx;
@@ -180,10 +192,15 @@ __global__ void __launch_bounds__(256) ce_merge_kernel(const float *__restrict__
   float sum = 0.f;
   if (live && M != -INFINITY) {
     const float mb = M * LOG2E;
-#pragma unroll 8
-    for (int p = q; p < P; p += 4) {
-      const float mp = wm[(int64_t)p * s];
-      if (mp != -INFINITY) sum += wse[(int64_t)p * s] * exp2f(fmaf(mp, LOG2E, -mb));
+    if (P <= 4 * U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (mv[u] != -INFINITY) sum += sv[u] * exp2f(fmaf(mv[u], LOG2E, -mb));
+    } else {
+      for (int p = q; p < P; p += 4) {
+        const float mp = wm[(int64_t)p * s];
+        if (mp != -INFINITY) sum += wse[(int64_t)p * s] * exp2f(fmaf(mp, LOG2E, -mb));
+      }
     }
   }
   part[1][q][lane] = sum;

@@ -85,7 +85,9 @@ def check_vs_unfused(got, ref):
 @pytest.mark.parametrize("s,h,Vs,start", [(136, 128, 200, 0), (300, 72, 1001, 2002), (64, 256, 1000, 5),
                                           (257, 64, 16032 // 4, 0), (5, 8, 1, 3), (9, 16, 0, 4),
                                           (10, 0, 50, 0), (520, 136, 2056, 77),
-                                          (40, 64, 40000, 1000)])  # 157 tile columns: uneven over the merge's 4 waves
+                                          (40, 64, 40000, 1000),  # 313 tile columns: the merge's general loop
+                                          (70, 64, 8192, 3),       # 64 tile columns: every load in registers
+                                          (70, 64, 8200, 5)])      # 65: the general loop
 def test_fused_small(oracle_mod, s, h, Vs, start):
     g = np.random.default_rng(s * 7 + Vs)
     Hf, W = bf(g.standard_normal((s, h))), bf(g.standard_normal((h, Vs)) * 0.05)
