@@ -3,14 +3,16 @@
 // output projections) in one launch, so that neither leaves CUs idle while the
 // other drains.  Kernels in gemm_bf16_kernels.h, dispatch in gemm_pair_impl.h.
 //
-// Supported pairs (first = the long-K product, second = the short-K one), both
+// Supported pairs (first = the product with the longer tiles, second = the other), both
 // with 16-byte-aligned operands and one residency: RES_TWO with 256-row tiles
 // of 256 or 192 columns, RES_WAVES8 with 256x256 tiles, RES_SHARED (two
 // workgroups per CU) with 128-row tiles of 192 or 128 columns:
 //   first  TN store (bf16) or TN split-K partial (fp32; gemm_pair_partial.hip);
 //   second NT store (also over K-segments), NT activation backward or NT SwiGLU
 //          backward;
-//   first  NN store, second NN store.
+//   first  NN store, second NN store;
+//   first  NT store or NT activation backward, second TN store (RES_WAVES8 and
+//          RES_SHARED; gemm_pair_nt.hip).
 #include "gemm_pair_impl.h"
 
 namespace {
@@ -52,6 +54,7 @@ hipError_t tp_launch_gemm_pair(const GemmDesc &d1, const GemmVariant &v1, const 
     if (v1.epi == EPI_STORE && !v1.out_f32) return first_tn<EPI_STORE, false>(d1, v1, d2, v2, red, dry, st);
     return hipErrorNotSupported;
   }
+  if (v1.layout == GEMM_NT) return tp_launch_gemm_pair_nt_first(d1, v1, d2, v2, red, dry, st);
   if (v1.layout == GEMM_NN && v1.epi == EPI_STORE && !v1.out_f32) {
     if (v1.res == RES_TWO) return first_nn<RES_TWO>(d1, v1, d2, v2, red, dry, st);
     if (v1.res == RES_WAVES8) return first_nn<RES_WAVES8>(d1, v1, d2, v2, red, dry, st);

@@ -58,6 +58,10 @@ hipError_t tp_launch_gemm_pair(const GemmDesc &d1, const GemmVariant &v1, const 
 // the pairs whose first product is a TN split-K partial (called by tp_launch_gemm_pair)
 hipError_t tp_launch_gemm_pair_tn_partial(const GemmDesc &d1, const GemmVariant &v1, const GemmDesc &d2,
                                           const GemmVariant &v2, const GemmDesc *red, bool dry, hipStream_t st);
+// the pairs whose first product is an NT activation gradient and whose second is
+// a TN weight gradient (called by tp_launch_gemm_pair)
+hipError_t tp_launch_gemm_pair_nt_first(const GemmDesc &d1, const GemmVariant &v1, const GemmDesc &d2,
+                                        const GemmVariant &v2, const GemmDesc *red, bool dry, hipStream_t st);
 
 // fp32 storage and arithmetic (64x64 tiles, any layout, any extents).
 constexpr int TP_F32_TILE = 64;

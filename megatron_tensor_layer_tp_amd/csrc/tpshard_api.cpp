@@ -569,15 +569,19 @@ int run(const Spec &s, const Ptrs &q, int dt, void *ws, hipStream_t st, const ch
 
 // Two independent products of one pass.  In bf16 they share one launch when
 // both plans fit the paired kernels: the first (long-K) product may be split
-// along K, the second is not.  Otherwise they run one after the other with
-// their own plans.  Plans depend on the sizes alone, so the workspace queries
-// see the same ones.
+// along K, the second is not.  With `swapped` the second product's blocks are
+// dispatched first and neither is split (a weight gradient s1 whose K, the
+// token count, is short beside the activation gradient s2).  Otherwise they
+// run one after the other with their own plans.  Plans depend on the sizes
+// alone, so the workspace queries see the same ones.
 struct PairPlan {
-  bool paired = false;
+  bool paired = false, swapped = false;
   Plan p1, p2;
 };
 
-PairPlan pair_plan(const Spec &s1, const Spec &s2, int dt) {
+enum PairMode { PAIR_AUTO, PAIR_OFF, PAIR_SWAP };
+
+PairPlan pair_plan_mode(const Spec &s1, const Spec &s2, int dt, PairMode mode) {
   PairPlan r;
   if (dt != TP_DT_BF16) {
     r.p1 = plan(s1, dt);
@@ -588,9 +592,9 @@ PairPlan pair_plan(const Spec &s1, const Spec &s2, int dt) {
   r.p1 = plan_bf16(s1);
   r.p2 = plan_bf16(s2);
   double best = plan_us(s1, r.p1) + plan_us(s2, r.p2);
-  // TP_GEMM_PAIR=off: always apart (timing comparisons; the parity tests use it
-  // to reach the single-launch paths of products that are normally paired)
-  if (const char *e = std::getenv("TP_GEMM_PAIR"); e != nullptr && std::strcmp(e, "off") == 0) return r;
+  if (mode == PAIR_OFF) return r;
+  const bool force_swap = mode == PAIR_SWAP;
+  if (force_swap) best = 1e30;
   // together: every built pair of variants with one residency, the first
   // possibly split along K
   Spec b = s2;
@@ -612,7 +616,7 @@ PairPlan pair_plan(const Spec &s1, const Spec &s2, int dt) {
                        std::max(tile_cost(p1.bm, p1.bn, p1.res).first, tile_cost(p2.bm, p2.bn, p2.res).first) +
                        list_makespan(n1, block_us(s1, p1, n1 + n2), n2, block_us(b, p2, n1 + n2), plan_slots(p1)) +
                        reduce_us(s1, p1);
-      if (t < best * 0.999) {
+      if (t < best * 0.999 && !force_swap) {
         best = t;
         r.paired = true;
         r.p1 = p1;
@@ -620,7 +624,43 @@ PairPlan pair_plan(const Spec &s1, const Spec &s2, int dt) {
       }
     }
   });
+  // swapped: s2's blocks first, neither split
+  Spec f = s2, a = s1;
+  f.can_split = false;
+  a.can_split = false;
+  std::vector<Plan> ca;
+  for_each_plan(a, [&](const Plan &p) { ca.push_back(p); });
+  for_each_plan(f, [&](const Plan &p2) {
+    for (const Plan &p1 : ca) {
+      if (!p1.vec || !p2.vec || p1.res != p2.res) continue;
+      if (tp_launch_gemm_pair(d2, variant(f, p2), d1, variant(a, p1), nullptr, true, nullptr) != hipSuccess) continue;
+      const int64_t n1 = plan_blocks(p1), n2 = plan_blocks(p2);
+      const double t = kLaunchUs +
+                       std::max(tile_cost(p1.bm, p1.bn, p1.res).first, tile_cost(p2.bm, p2.bn, p2.res).first) +
+                       list_makespan(n2, block_us(f, p2, n1 + n2), n1, block_us(a, p1, n1 + n2), plan_slots(p2));
+      if (t < best * 0.999) {
+        best = t;
+        r.paired = r.swapped = true;
+        r.p1 = p1;
+        r.p2 = p2;
+      }
+    }
+  });
   return r;
+}
+
+// TP_GEMM_PAIR=off: always apart (timing comparisons; the parity tests use it
+// to reach the single-launch paths of products that are normally paired);
+// TP_GEMM_PAIR=swap: the swapped order whenever a pair of variants is built for
+// it, else the usual choice (the parity tests reach its kernels at small sizes)
+PairPlan pair_plan(const Spec &s1, const Spec &s2, int dt) {
+  const char *env = std::getenv("TP_GEMM_PAIR");
+  if (env != nullptr && std::strcmp(env, "off") == 0) return pair_plan_mode(s1, s2, dt, PAIR_OFF);
+  if (env != nullptr && std::strcmp(env, "swap") == 0 && dt == TP_DT_BF16) {
+    const PairPlan r = pair_plan_mode(s1, s2, dt, PAIR_SWAP);
+    if (r.swapped) return r;
+  }
+  return pair_plan_mode(s1, s2, dt, PAIR_AUTO);
 }
 
 size_t pair_ws_bytes(const Spec &s1, const Spec &s2, int dt) {
@@ -654,11 +694,12 @@ int run_pair(const Spec &s1, const Ptrs &q1, const Spec &s2, const Ptrs &q2, int
     return run_planned(s2, pp.p2, q2, dt, ws, st, what2);
   }
   if (pp.p1.splits > 1 && ws == nullptr) return fail(TP_EWORKSPACE, "%s: split-K plan without workspace", what1);
-  log_plan(what1, s1, pp.p1, " (paired, first)");
-  log_plan(what2, s2, pp.p2, " (paired, second)");
+  log_plan(what1, s1, pp.p1, pp.swapped ? " (paired, second)" : " (paired, first)");
+  log_plan(what2, s2, pp.p2, pp.swapped ? " (paired, first)" : " (paired, second)");
   const GemmDesc d1 = make_desc(s1, q1, pp.p1, dt, ws);
   const GemmDesc d2 = make_desc(s2, q2, pp.p2, dt, nullptr);
-  hipError_t e = tp_launch_gemm_pair(d1, variant(s1, pp.p1), d2, variant(s2, pp.p2), red, false, st);
+  hipError_t e = pp.swapped ? tp_launch_gemm_pair(d2, variant(s2, pp.p2), d1, variant(s1, pp.p1), red, false, st)
+                            : tp_launch_gemm_pair(d1, variant(s1, pp.p1), d2, variant(s2, pp.p2), red, false, st);
   if (red != nullptr) in->on = false;
   if (e == hipSuccess && pp.p1.splits > 1) {
     if (out != nullptr && !s1.out_f32 && pp.p1.vec) {
