@@ -21,13 +21,17 @@
  *    on one shard; the caller passes that shard's slices and sizes.
  *  - Pointers X, W*, Z, ... are DEVICE pointers owned by the caller.  The
  *    library allocates no memory, frees nothing and keeps no state between
- *    calls.  Every pointer must be 16-byte aligned (TP_EALIGN otherwise).
+ *    calls (the one exception, the device array of tp_lm_head_ce_fwd_noalloc,
+ *    is described there).  Every pointer must be 16-byte aligned (TP_EALIGN
+ *    otherwise).
  *    Outputs are overwritten (never accumulated into) and must not alias any
  *    input or each other.  Inputs are never modified.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *    enqueue work and return; results are valid once the caller synchronizes
  *    the stream.  Calls on different streams may run concurrently when their
- *    outputs and workspaces are distinct.
+ *    outputs and workspaces are distinct.  No call synchronizes, allocates or
+ *    clears memory with hipMemsetAsync, so a sequence of calls can be captured
+ *    into a HIP graph and replayed with the same pointers and sizes.
  *  - Every argument is checked before anything is enqueued: on an error no
  *    kernel runs, the call returns the status and tp_last_error() (per host
  *    thread) says which check failed.  A failed launch returns TP_EHIP.
@@ -40,7 +44,8 @@
  *    saved activations, gradients), fp32 accumulation, round-to-nearest-even
  *    on every store.  TP_DT_F32: fp32 storage and arithmetic throughout.
  *  - Thread safety: the library holds no shared mutable state except the
- *    per-thread last-error string.
+ *    per-thread last-error string and the per-device array of
+ *    tp_lm_head_ce_fwd_noalloc.
  */
 #ifndef TPSHARD_H
 #define TPSHARD_H
