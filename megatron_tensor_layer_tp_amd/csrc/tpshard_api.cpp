@@ -368,6 +368,10 @@ struct Ptrs {
   int stream_out = 0;  // GemmDesc::stream_out
 };
 
+// tile rows per group of the launch's tile order (the kernels walk a group's
+// columns, XCD by XCD)
+constexpr int kGroupM = 8;
+
 GemmDesc make_desc(const Spec &s, const Ptrs &q, const Plan &p, int dt, void *ws) {
   GemmDesc d;
   std::memset(&d, 0, sizeof d);
@@ -406,7 +410,7 @@ GemmDesc make_desc(const Spec &s, const Ptrs &q, const Plan &p, int dt, void *ws
   d.kt_per_split = p.kt_per_split;
   d.tiles_m = p.tiles_m;
   d.tiles_n = p.tiles_n;
-  d.group_m = 8;
+  d.group_m = kGroupM;
   d.ws = (float *)ws;
   d.stream_out = q.stream_out;
   return d;
@@ -472,7 +476,7 @@ Tail plan_tail(const Spec &s, const Plan &p) {
   int a = p.tiles_m, b = -1, c = p.tiles_n, e = -1;
   for (int i = T - rem; i < T; ++i) {
     int tm, tn;
-    tile_rc(p.tiles_m, p.tiles_n, 8, i, tm, tn);
+    tile_rc(p.tiles_m, p.tiles_n, kGroupM, i, tm, tn);
     a = std::min(a, tm);
     b = std::max(b, tm);
     c = std::min(c, tn);
