@@ -105,7 +105,8 @@ size_t tp_mlp_bwd_workspace(int dt, int64_t s, int64_t h, int64_t ft);
  * Z and H are the forward's outputs for the same X, W1 (Z may be NULL for
  * ReLU, then the mask is H > 0).  dY [s,h] is the full output gradient
  * (g's backward is the identity).  ws / ws_bytes: device workspace of at least
- * tp_mlp_bwd_workspace() bytes, 256-byte aligned; its contents on entry do not
+ * tp_mlp_bwd_workspace() bytes, 256-byte aligned (NULL when that is 0: the
+ * planned launches split no product along K); its contents on entry do not
  * matter and are garbage on return. */
 int tp_mlp_bwd(int act, int dt, int64_t s, int64_t h, int64_t ft,
                const void *X, const void *W1, const void *W2,
